@@ -1,0 +1,196 @@
+"""Plain CPU oracle for the Kimi Delta Attention (KDA) recurrence.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+library (no helpers, tables, constants or pre/post-processing).
+
+What it computes (the plain definition, token by token, in float64):
+
+* Gate -- vLLM PR #55737 "Use FlashKDA for KDA chunked prefill", opening
+  commit message and the "Purpose" section: the bounded gate is
+  ``lower_bound * sigmoid(exp(A_log) * (g + dt_bias))``; q and k are
+  L2-normalised inside the kernel; beta arrives as raw logits.  We read the
+  gate value as the natural log of the per-key-channel decay alpha, so
+  alpha = exp(gate) lies in [exp(lower_bound), 1].
+* Recurrence -- the same page states that FlashKDA and the Triton chunk path
+  compute one and the same bounded-gate KDA recurrence, but no page writes the
+  step out.  The step used here is the gated delta rule with a per-key-channel
+  gate: decay the rows of the state S[K, V] by alpha, apply the delta rule
+  on the decayed state, then read the output from the updated state:
+      S <- Diag(alpha) S
+      S <- S + beta * k (v - S^T k)^T
+      o  = scale * S^T q
+* Verify -- TensorRT-LLM PR #21179 "GLM-5.3-Flash FP8 performance fixes on
+  Hopper", the fused-verify commit message: one call seeds each batch row from
+  the state pool and writes step t's state to row (b, t) of the per-step state
+  buffer; the pool stays read-only.  Reading used: row t holds the state after
+  token t (0-based), so the last row is the all-accepted state.
+
+Readings taken where the pages are silent:
+L2 norm is x / sqrt(sum(x^2) + 1e-6); scale defaults to 1/sqrt(d_k); state
+layout is [K, V] (rows are key channels, the ones the gate decays); a
+zero-length sequence leaves its state untouched; a negative state index marks
+a padding row whose outputs are zero and whose states are not written.
+
+Parity pins for every function here live in ``tests/test_oracle_pins.py``.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+L2NORM_EPS = 1e-6
+
+
+# ---------------------------------------------------------------------------
+# Elementwise pieces (vLLM PR #55737, opening commit / "Purpose")
+# ---------------------------------------------------------------------------
+
+def sigmoid(x):
+    """Logistic function in float64, written in the overflow-free two-branch form."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    pos = x >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-x[pos]))
+    ex = np.exp(x[~pos])
+    out[~pos] = ex / (1.0 + ex)
+    return out
+
+
+def l2_normalize(x, eps: float = L2NORM_EPS):
+    """Row-wise x / sqrt(sum(x^2) + eps) over the last axis (q/k L2 norm)."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
+
+
+def gate_log_alpha(g, A_log, dt_bias, lower_bound: float):
+    """Bounded gate: lower_bound * sigmoid(exp(A_log) * (g + dt_bias)).
+
+    g: [..., H, K]; A_log: [H]; dt_bias: [H, K].  Returns log(alpha) with the
+    same shape as g (natural log, per key channel).
+    """
+    g = np.asarray(g, dtype=np.float64)
+    a = np.exp(np.asarray(A_log, dtype=np.float64))[:, None]          # [H, 1]
+    return float(lower_bound) * sigmoid(a * (g + np.asarray(dt_bias, np.float64)))
+
+
+def beta_from_logits(beta_logits):
+    """beta = sigmoid(beta logit); the kernel receives logits (vLLM PR #55737)."""
+    return sigmoid(beta_logits)
+
+
+# ---------------------------------------------------------------------------
+# One recurrence step (the definition).  Works on float64 arrays and, for the
+# exact brute-force pins, on object arrays of fractions.Fraction.
+# ---------------------------------------------------------------------------
+
+def kda_step(S, q_hat, k_hat, v, alpha, beta, scale):
+    """One token of the gated delta rule for a batch of independent heads.
+
+    S: [B, K, V]; q_hat, k_hat, alpha: [B, K]; v: [B, V]; beta: [B].
+    Returns (S_new, o) with o: [B, V].
+    """
+    S = alpha[:, :, None] * S                                      # S <- Diag(alpha) S
+    r = np.einsum("bkv,bk->bv", S, k_hat)                          # S^T k
+    S = S + beta[:, None, None] * k_hat[:, :, None] * (v - r)[:, None, :]
+    o = scale * np.einsum("bkv,bk->bv", S, q_hat)                  # o = scale S^T q
+    return S, o
+
+
+# ---------------------------------------------------------------------------
+# Modes
+# ---------------------------------------------------------------------------
+
+def _as64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def chunk_prefill(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, cu_seqlens,
+                  initial_state=None, initial_state_idx=None, scale=None):
+    """Varlen prefill, token by token.
+
+    q, k, g: [T_total, H, K]; v: [T_total, H, V]; beta_logits: [T_total, H];
+    A_log: [H]; dt_bias: [H, K]; cu_seqlens: [N+1] ints (cu[0] = 0, non-decreasing).
+    initial_state: None (zeros) or [rows, H, K, V]; row n is used for sequence n,
+    or row initial_state_idx[n] when an index vector is given.
+    Returns (out [T_total, H, V] float64, final_state [N, H, K, V] float64).
+    """
+    q, k, v, g = _as64(q), _as64(k), _as64(v), _as64(g)
+    T_total, H, K = q.shape
+    V = v.shape[-1]
+    cu = [int(c) for c in np.asarray(cu_seqlens).reshape(-1)]
+    N = len(cu) - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    out = np.zeros((T_total, H, V), dtype=np.float64)
+    final = np.zeros((N, H, K, V), dtype=np.float64)
+
+    qn = l2_normalize(q)
+    kn = l2_normalize(k)
+    alpha = np.exp(gate_log_alpha(g, A_log, dt_bias, lower_bound))
+    beta = beta_from_logits(_as64(beta_logits))
+
+    # Sequences of equal length are stepped together (they are independent).
+    by_len = {}
+    for n in range(N):
+        by_len.setdefault(cu[n + 1] - cu[n], []).append(n)
+    for length, seqs in by_len.items():
+        S = np.zeros((len(seqs), H, K, V), dtype=np.float64)
+        if initial_state is not None:
+            init = _as64(initial_state)
+            for j, n in enumerate(seqs):
+                row = n if initial_state_idx is None else int(initial_state_idx[n])
+                S[j] = init[row]
+        S = S.reshape(len(seqs) * H, K, V)
+        starts = np.array([cu[n] for n in seqs])
+        for t in range(length):
+            rows = starts + t
+            S, o = kda_step(S, qn[rows].reshape(-1, K), kn[rows].reshape(-1, K),
+                            v[rows].reshape(-1, V), alpha[rows].reshape(-1, K),
+                            beta[rows].reshape(-1), scale)
+            out[rows] = o.reshape(len(seqs), H, V)
+        final[seqs] = S.reshape(len(seqs), H, K, V)
+    return out, final
+
+
+def recurrent_verify(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound,
+                     state_pool, state_idx, num_steps, scale=None):
+    """Multi-step verify: B rows of num_steps tokens each (token b*T + t).
+
+    state_pool: [slots, H, K, V] (read only); state_idx: [B] ints, negative = padding.
+    Returns (out [B*T, H, V], intermediate [B, T, H, K, V]) where
+    intermediate[b, t] is the state after token t of row b.  Padding rows give
+    zero outputs and zero intermediate rows (the GPU leaves them unwritten).
+    """
+    q, k, v, g = _as64(q), _as64(k), _as64(v), _as64(g)
+    BT, H, K = q.shape
+    V = v.shape[-1]
+    T = int(num_steps)
+    B = BT // T
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    idx = np.asarray(state_idx).reshape(-1)
+    out = np.zeros((BT, H, V), dtype=np.float64)
+    inter = np.zeros((B, T, H, K, V), dtype=np.float64)
+    live = [b for b in range(B) if int(idx[b]) >= 0]
+    if not live:
+        return out, inter
+    pool = np.asarray(state_pool)
+    S = np.stack([pool[int(idx[b])].astype(np.float64) for b in live]).reshape(-1, K, V)
+
+    qn = l2_normalize(q)
+    kn = l2_normalize(k)
+    alpha = np.exp(gate_log_alpha(g, A_log, dt_bias, lower_bound))
+    beta = beta_from_logits(_as64(beta_logits))
+    live_arr = np.array(live)
+    for t in range(T):
+        rows = live_arr * T + t
+        S, o = kda_step(S, qn[rows].reshape(-1, K), kn[rows].reshape(-1, K),
+                        v[rows].reshape(-1, V), alpha[rows].reshape(-1, K),
+                        beta[rows].reshape(-1), scale)
+        out[rows] = o.reshape(len(live), H, V)
+        inter[live_arr, t] = S.reshape(len(live), H, K, V)
+    return out, inter
