@@ -1,0 +1,150 @@
+/*
+ * libkda -- Kimi Delta Attention (KDA) on AMD Instinct MI355X (gfx950).
+ *
+ * The recurrence (per sequence, per head; state S is [K][V] fp32, rows are key
+ * channels):
+ *     q^ = q / sqrt(sum q^2 + 1e-6),  k^ = k / sqrt(sum k^2 + 1e-6)
+ *     log alpha = lower_bound * sigmoid(exp(A_log[h]) * (g + dt_bias[h]))   (per key channel)
+ *     beta      = sigmoid(beta_logit)
+ *     S <- Diag(alpha) S;   S <- S + beta k^ (v - S^T k^)^T;   o = scale * S^T q^
+ * The gate, the in-kernel q/k L2 norm and the raw beta logits are those of
+ * vLLM PR #55737 "Use FlashKDA for KDA chunked prefill" (opening commit
+ * message, "Purpose").  The one-launch multi-step verify with a read-only
+ * state pool and one state row per draft step is that of TensorRT-LLM PR
+ * #21179 "GLM-5.3-Flash FP8 performance fixes on Hopper" (fused-verify commit
+ * message).  Supported shapes follow the same vLLM page: bf16 inputs,
+ * head_dim 128, bounded gate.
+ *
+ * Conventions shared by every entry point:
+ *  - Every buffer is caller-owned device memory.  The library never allocates
+ *    or frees memory, never synchronises a stream and never reads device
+ *    memory from the host.  Work is enqueued on `stream` (a hipStream_t cast
+ *    to void*, NULL = the default stream) and is asynchronous.
+ *  - bf16 tensors are passed as raw 16-bit words (void*), laid out token-major:
+ *    element (token t, head h, channel c) sits at t*token_stride + h*128 + c.
+ *    A token stride of 0 means the dense default (H*128, or H for beta logits);
+ *    larger strides read rows in place from a fused projection.
+ *  - States are fp32 [.., H, 128 (key), 128 (value)] row-major, value channel
+ *    contiguous.
+ *  - Only host-side arguments are validated; a failed check returns a status
+ *    and sets a thread-local message (kda_last_error) without enqueuing work.
+ *    Device-side contents (cu_seqlens monotone with cu[0] = 0 and
+ *    cu[N] == total_tokens, indices in range, finite inputs) are preconditions.
+ *  - Results are deterministic run to run (no atomics).
+ *  - fp16 is used for intermediate MFMA operands in prefill: values of v and
+ *    of the state must stay below 2^14 in magnitude.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+#define KDA_HEAD_DIM 128
+#define KDA_MAX_VERIFY_STEPS 64
+
+typedef enum kda_status {
+  KDA_OK = 0,
+  KDA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative size, bad stride, overlap */
+  KDA_ERR_UNSUPPORTED = 2,        /* head_dim != 128, lower_bound outside [-5, 0], too many steps */
+  KDA_ERR_WORKSPACE_TOO_SMALL = 3,
+  KDA_ERR_HIP = 4                 /* a HIP runtime call or a kernel launch failed */
+} kda_status;
+
+/* Shapes and strides of one prefill call.  All values are host integers:
+ * nothing is read back from the device (the lesson of TensorRT-LLM PR #21179,
+ * host cu_seqlens commit: a device read of chunk counts stalls every layer). */
+typedef struct kda_prefill_desc {
+  int32_t num_seqs;          /* N; cu_seqlens holds N+1 entries */
+  int32_t total_tokens;      /* T_total == cu_seqlens[N] */
+  int32_t num_heads;         /* H >= 1 */
+  int32_t head_dim;          /* must be 128 */
+  float scale;               /* output scale; <= 0 selects 1/sqrt(128) */
+  int32_t num_state_rows;    /* rows of initial_state (N when indexed directly, pool slots when indexed) */
+  int64_t q_token_stride, k_token_stride, v_token_stride, g_token_stride;  /* elements, 0 = H*128 */
+  int64_t beta_token_stride; /* elements, 0 = H */
+  int64_t out_token_stride;  /* elements, 0 = H*128 */
+} kda_prefill_desc;
+
+typedef struct kda_verify_desc {
+  int32_t batch;             /* B rows; token of row b, step t is b*num_steps + t */
+  int32_t num_steps;         /* T draft steps per row, 1..KDA_MAX_VERIFY_STEPS */
+  int32_t num_heads;         /* H */
+  int32_t head_dim;          /* must be 128 */
+  float scale;               /* <= 0 selects 1/sqrt(128) */
+  int32_t num_slots;         /* rows of state_pool */
+  int64_t q_token_stride, k_token_stride, v_token_stride, g_token_stride;
+  int64_t beta_token_stride;
+  int64_t out_token_stride;
+} kda_verify_desc;
+
+/* Bytes of caller-provided workspace kda_chunk_prefill needs for these shapes.
+ * Returns 0 for shapes the library does not support. */
+size_t kda_chunk_prefill_workspace_size(int32_t num_seqs, int32_t total_tokens,
+                                        int32_t num_heads, int32_t head_dim);
+
+/*
+ * Varlen chunked prefill of N packed sequences (vLLM PR #55737, the FlashKDA
+ * role: output written straight into the caller's layer buffer, final state
+ * returned).
+ *   q, k, g, v      bf16 [T_total, H, 128] (token-strided, see desc)
+ *   beta_logits     bf16 [T_total, H], raw logits
+ *   A_log           fp32 [H];  dt_bias fp32 [H, 128]
+ *   lower_bound     finite, in [-5, 0]
+ *   cu_seqlens      device int32 [N+1]
+ *   initial_state   fp32 [num_state_rows, H, 128, 128] or NULL (zero start)
+ *   initial_state_idx  device int32 [N] or NULL.  When given, sequence n starts
+ *                   from initial_state[initial_state_idx[n]]; an index < 0 or
+ *                   >= num_state_rows starts from zero.  When NULL, sequence n
+ *                   starts from initial_state[n].
+ *   out             bf16 [T_total, H, 128]; must not overlap any input
+ *   final_state     fp32 [N, H, 128, 128] or NULL (not written).  May alias
+ *                   initial_state when both are indexed the same way.
+ *   workspace       device scratch of at least kda_chunk_prefill_workspace_size bytes.
+ * A zero-length sequence writes no output and copies its start state to final_state.
+ */
+kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const void* g,
+                             const void* beta_logits, const float* A_log, const float* dt_bias,
+                             float lower_bound, const int32_t* cu_seqlens,
+                             const float* initial_state, const int32_t* initial_state_idx,
+                             void* out, float* final_state,
+                             void* workspace, size_t workspace_bytes,
+                             const kda_prefill_desc* desc, void* stream);
+
+/*
+ * Fused multi-step verify (TensorRT-LLM PR #21179, fused-verify commit: the
+ * fused_recurrent_kda role).  For each row b the state starts from
+ * state_pool[state_idx[b]] (the pool is only read) and the T tokens of the row
+ * are applied in order.
+ *   q, k, g, v      bf16 [B*T, H, 128];  beta_logits bf16 [B*T, H]
+ *   state_pool      fp32 [num_slots, H, 128, 128], read only
+ *   state_idx       device int32 [B]; an index < 0 or >= num_slots marks a
+ *                   padding row: its outputs are written as zeros and its
+ *                   intermediate rows are left untouched.
+ *   intermediate_state  fp32 [B, T, H, 128, 128]; row (b, t) receives the state
+ *                   after token t of row b (0-based), so row (b, T-1) is the
+ *                   state with every draft token accepted.  Must not overlap the pool.
+ *   out             bf16 [B*T, H, 128]
+ */
+kda_status kda_recurrent_verify(const void* q, const void* k, const void* v, const void* g,
+                                const void* beta_logits, const float* A_log, const float* dt_bias,
+                                float lower_bound, const float* state_pool,
+                                const int32_t* state_idx, float* intermediate_state, void* out,
+                                const kda_verify_desc* desc, void* stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* kda_last_error(void);
+
+/* KDA_ABI_VERSION of the loaded library. */
+int kda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -1,0 +1,248 @@
+"""ctypes binding for libkda: argument marshalling only.
+
+Every step of the KDA path runs in the library's HIP kernels; this module
+checks torch dtypes/devices/shapes, turns tensors into pointers and strides,
+passes torch's current HIP stream, and raises on a non-OK status.  torch is
+used only for device memory and streams.  There is no CPU fallback: if the
+library is missing, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkda.so")
+HEADER_PATH = os.path.join(os.path.dirname(HERE), "include", "kda.h")
+HEAD_DIM = 128
+
+KDA_OK = 0
+STATUS_NAMES = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
+                3: "KDA_ERR_WORKSPACE_TOO_SMALL", 4: "KDA_ERR_HIP"}
+
+
+class PrefillDesc(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("total_tokens", ctypes.c_int32),
+                ("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("num_state_rows", ctypes.c_int32),
+                ("q_token_stride", ctypes.c_int64), ("k_token_stride", ctypes.c_int64),
+                ("v_token_stride", ctypes.c_int64), ("g_token_stride", ctypes.c_int64),
+                ("beta_token_stride", ctypes.c_int64), ("out_token_stride", ctypes.c_int64)]
+
+
+class VerifyDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_steps", ctypes.c_int32),
+                ("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("num_slots", ctypes.c_int32),
+                ("q_token_stride", ctypes.c_int64), ("k_token_stride", ctypes.c_int64),
+                ("v_token_stride", ctypes.c_int64), ("g_token_stride", ctypes.c_int64),
+                ("beta_token_stride", ctypes.c_int64), ("out_token_stride", ctypes.c_int64)]
+
+
+_lib = None
+
+
+class KDAError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def load_library(path: str | None = None):
+    """Load libkda.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"libkda is not built ({path} missing); run "
+                           "`python -m linear_attention_rule_amd.build` first")
+    lib = ctypes.CDLL(path)
+    vp, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+    lib.kda_abi_version.restype = ctypes.c_int
+    lib.kda_abi_version.argtypes = []
+    lib.kda_last_error.restype = ctypes.c_char_p
+    lib.kda_last_error.argtypes = []
+    lib.kda_chunk_prefill_workspace_size.restype = sz
+    lib.kda_chunk_prefill_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.kda_chunk_prefill.restype = ctypes.c_int
+    lib.kda_chunk_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, vp, sz,
+                                      ctypes.POINTER(PrefillDesc), vp]
+    lib.kda_recurrent_verify.restype = ctypes.c_int
+    lib.kda_recurrent_verify.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp,
+                                         ctypes.POINTER(VerifyDesc), vp]
+    if lib.kda_abi_version() != 1:
+        raise RuntimeError("libkda ABI version mismatch")
+    _lib = lib
+    return lib
+
+
+def header_entry_points() -> list[str]:
+    """Names of the functions include/kda.h declares."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(status):
+    if status != KDA_OK:
+        raise KDAError(status, _lib.kda_last_error().decode())
+
+
+def _token_tensor(name, t, heads, width):
+    """A [tokens, heads, width] (or [tokens, heads] when width is None) view with dense heads."""
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if width is None:
+        if t.dim() != 2 or t.shape[1] != heads:
+            raise ValueError(f"{name} must be [tokens, {heads}]")
+        if t.numel() == 0:
+            return 0
+        if t.stride(1) != 1:
+            raise ValueError(f"{name} must have contiguous heads")
+    else:
+        if t.dim() != 3 or t.shape[1] != heads or t.shape[2] != width:
+            raise ValueError(f"{name} must be [tokens, {heads}, {width}]")
+        if t.numel() == 0:
+            return 0
+        if t.stride(2) != 1 or t.stride(1) != width:
+            raise ValueError(f"{name} must have dense heads")
+    return t.stride(0)
+
+
+def _f32(name, t, shape):
+    if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous float32 device tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _i32(name, t, n):
+    if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous() or t.dim() != 1:
+        raise TypeError(f"{name} must be a contiguous 1-D int32 device tensor")
+    if n is not None and t.numel() != n:
+        raise ValueError(f"{name} must have {n} entries")
+
+
+def prefill_workspace_bytes(num_seqs: int, total_tokens: int, num_heads: int) -> int:
+    lib = load_library()
+    return int(lib.kda_chunk_prefill_workspace_size(num_seqs, total_tokens, num_heads, HEAD_DIM))
+
+
+def chunk_prefill(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, cu_seqlens, *,
+                  initial_state=None, initial_state_idx=None, out=None, final_state=None,
+                  write_final_state=True, scale=None, workspace=None, check=False):
+    """Varlen chunked KDA prefill.  Returns (out, final_state or None).
+
+    q, k, v, g: bf16 [T, H, 128] (token stride free, heads dense); beta_logits bf16 [T, H];
+    A_log f32 [H]; dt_bias f32 [H, 128]; cu_seqlens int32 [N+1] on the device.
+    N comes from cu_seqlens.numel() and T from q.shape[0]: both host values.
+    """
+    lib = load_library()
+    T, H = int(q.shape[0]), int(q.shape[1])
+    N = int(cu_seqlens.numel()) - 1
+    qs = _token_tensor("q", q, H, HEAD_DIM)
+    ks = _token_tensor("k", k, H, HEAD_DIM)
+    vs = _token_tensor("v", v, H, HEAD_DIM)
+    gs = _token_tensor("g", g, H, HEAD_DIM)
+    bs = _token_tensor("beta_logits", beta_logits, H, None)
+    for name, t in (("k", k), ("v", v), ("g", g), ("beta_logits", beta_logits)):
+        if t.shape[0] != T:
+            raise ValueError(f"{name} has {t.shape[0]} tokens, q has {T}")
+    _f32("A_log", A_log, (H,))
+    _f32("dt_bias", dt_bias, (H, HEAD_DIM))
+    _i32("cu_seqlens", cu_seqlens, None)
+    if N < 0:
+        raise ValueError("cu_seqlens needs at least one entry")
+    dev = q.device
+    rows = 0
+    if initial_state is not None:
+        if initial_state.dim() != 4:
+            raise ValueError("initial_state must be [rows, H, 128, 128]")
+        rows = int(initial_state.shape[0])
+        _f32("initial_state", initial_state, (rows, H, HEAD_DIM, HEAD_DIM))
+    if initial_state_idx is not None:
+        _i32("initial_state_idx", initial_state_idx, N)
+    if out is None:
+        out = torch.empty((T, H, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+    os_ = _token_tensor("out", out, H, HEAD_DIM)
+    if out.shape[0] != T:
+        raise ValueError("out must have T tokens")
+    if final_state is None and write_final_state:
+        final_state = torch.empty((N, H, HEAD_DIM, HEAD_DIM), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _f32("final_state", final_state, (N, H, HEAD_DIM, HEAD_DIM))
+    need = int(lib.kda_chunk_prefill_workspace_size(N, T, H, HEAD_DIM))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if check:
+        cu = cu_seqlens.cpu()
+        if int(cu[0]) != 0 or int(cu[-1]) != T or bool((cu[1:] < cu[:-1]).any()):
+            raise ValueError("cu_seqlens must start at 0, be non-decreasing and end at T")
+    desc = PrefillDesc(N, T, H, HEAD_DIM, float(scale) if scale else 0.0, rows,
+                       qs, ks, vs, gs, bs, os_)
+    st = lib.kda_chunk_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta_logits), _ptr(A_log),
+                               _ptr(dt_bias), float(lower_bound), _ptr(cu_seqlens),
+                               _ptr(initial_state), _ptr(initial_state_idx), _ptr(out),
+                               _ptr(final_state), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), ctypes.byref(desc),
+                               _stream_handle(dev))
+    _check(st)
+    return out, final_state
+
+
+def recurrent_verify(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, state_pool, state_idx,
+                     num_steps, *, intermediate=None, out=None, scale=None):
+    """Fused multi-step verify.  Returns (out [B*T, H, 128] bf16, intermediate [B, T, H, 128, 128] f32)."""
+    lib = load_library()
+    BT, H = int(q.shape[0]), int(q.shape[1])
+    T = int(num_steps)
+    if T < 1 or BT % T:
+        raise ValueError("token count must be a multiple of num_steps")
+    B = BT // T
+    qs = _token_tensor("q", q, H, HEAD_DIM)
+    ks = _token_tensor("k", k, H, HEAD_DIM)
+    vs = _token_tensor("v", v, H, HEAD_DIM)
+    gs = _token_tensor("g", g, H, HEAD_DIM)
+    bs = _token_tensor("beta_logits", beta_logits, H, None)
+    _f32("A_log", A_log, (H,))
+    _f32("dt_bias", dt_bias, (H, HEAD_DIM))
+    slots = int(state_pool.shape[0])
+    _f32("state_pool", state_pool, (slots, H, HEAD_DIM, HEAD_DIM))
+    _i32("state_idx", state_idx, B)
+    dev = q.device
+    if out is None:
+        out = torch.empty((BT, H, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+    os_ = _token_tensor("out", out, H, HEAD_DIM)
+    if intermediate is None:
+        intermediate = torch.empty((B, T, H, HEAD_DIM, HEAD_DIM), dtype=torch.float32, device=dev)
+    _f32("intermediate", intermediate, (B, T, H, HEAD_DIM, HEAD_DIM))
+    desc = VerifyDesc(B, T, H, HEAD_DIM, float(scale) if scale else 0.0, slots,
+                      qs, ks, vs, gs, bs, os_)
+    st = lib.kda_recurrent_verify(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta_logits),
+                                  _ptr(A_log), _ptr(dt_bias), float(lower_bound), _ptr(state_pool),
+                                  _ptr(state_idx), _ptr(intermediate), _ptr(out),
+                                  ctypes.byref(desc), _stream_handle(dev))
+    _check(st)
+    return out, intermediate
+
+
+def default_scale() -> float:
+    return 1.0 / math.sqrt(HEAD_DIM)

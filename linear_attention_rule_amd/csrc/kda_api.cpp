@@ -1,0 +1,234 @@
+// libkda C ABI: host-side validation, workspace sizing and kernel launches.
+//
+// Every check here uses host integers only (shapes, strides, pointer values);
+// no device memory is read and no stream is synchronised, so a call can be
+// captured into a HIP graph.  Status codes and messages follow include/kda.h.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kda_status fail(kda_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+kda_status ok() {
+  g_last_error.clear();
+  return KDA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Span {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+// Bytes touched by a token-strided tensor of `tokens` rows of `row_elems` elements.
+Span span_of(const void* base, int64_t tokens, int64_t stride, int64_t row_elems, int64_t esize) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(base);
+  if (tokens <= 0) return {lo, lo};
+  return {lo, lo + static_cast<uintptr_t>(((tokens - 1) * stride + row_elems) * esize)};
+}
+
+bool overlaps(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+// Validates one token-strided bf16 input: returns the effective stride (0 -> dense default).
+kda_status check_stride(const char* name, int64_t stride, int64_t dense, int64_t row_elems,
+                        int64_t* eff) {
+  if (stride == 0) stride = dense;
+  if (stride < row_elems) return fail(KDA_ERR_INVALID_ARGUMENT, "%s token stride %lld < %lld", name,
+                                      static_cast<long long>(stride), static_cast<long long>(row_elems));
+  *eff = stride;
+  return KDA_OK;
+}
+
+kda_status check_lower_bound(float lb) {
+  if (!std::isfinite(lb)) return fail(KDA_ERR_UNSUPPORTED, "lower_bound must be finite");
+  // The intra-chunk factorisation keeps every exponential of a 16-token block
+  // within fp32/bf16 range only while 16 * |lower_bound| * log2(e) < 127.
+  if (lb < -5.0f || lb > 0.0f)
+    return fail(KDA_ERR_UNSUPPORTED, "lower_bound %g outside the supported range [-5, 0]", lb);
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_last_error(void) { return g_last_error.c_str(); }
+
+size_t kda_chunk_prefill_workspace_size(int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
+                                        int32_t head_dim) {
+  if (num_seqs < 0 || total_tokens < 0 || num_heads < 1 || head_dim != KDA_HEAD_DIM) return 0;
+  return static_cast<size_t>(kda::chunk_slots(num_seqs, total_tokens)) *
+         static_cast<size_t>(num_heads) * static_cast<size_t>(kda::REC_BYTES);
+}
+
+kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const void* g,
+                             const void* beta_logits, const float* A_log, const float* dt_bias,
+                             float lower_bound, const int32_t* cu_seqlens,
+                             const float* initial_state, const int32_t* initial_state_idx,
+                             void* out, float* final_state, void* workspace,
+                             size_t workspace_bytes, const kda_prefill_desc* desc, void* stream) {
+  if (!desc) return fail(KDA_ERR_INVALID_ARGUMENT, "desc is NULL");
+  const int N = desc->num_seqs, T = desc->total_tokens, H = desc->num_heads;
+  if (desc->head_dim != KDA_HEAD_DIM)
+    return fail(KDA_ERR_UNSUPPORTED, "head_dim %d unsupported (only 128)", desc->head_dim);
+  if (N < 0 || T < 0 || H < 1)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "bad sizes N=%d T_total=%d H=%d", N, T, H);
+  if (kda_status s = check_lower_bound(lower_bound)) return s;
+  if (!A_log || !dt_bias) return fail(KDA_ERR_INVALID_ARGUMENT, "A_log / dt_bias is NULL");
+  if (N > 0 && !cu_seqlens) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL");
+  if (T > 0 && (!q || !k || !v || !g || !beta_logits || !out))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "an input or output pointer is NULL");
+  if (initial_state_idx && !initial_state)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "initial_state_idx given without initial_state");
+  if (initial_state && desc->num_state_rows < (initial_state_idx ? 1 : N))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "num_state_rows %d too small", desc->num_state_rows);
+  const int64_t HD = static_cast<int64_t>(H) * KDA_HEAD_DIM;
+  int64_t qs, ks, vs, gs, bs, os;
+  if (kda_status s = check_stride("q", desc->q_token_stride, HD, HD, &qs)) return s;
+  if (kda_status s = check_stride("k", desc->k_token_stride, HD, HD, &ks)) return s;
+  if (kda_status s = check_stride("v", desc->v_token_stride, HD, HD, &vs)) return s;
+  if (kda_status s = check_stride("g", desc->g_token_stride, HD, HD, &gs)) return s;
+  if (kda_status s = check_stride("beta_logits", desc->beta_token_stride, H, H, &bs)) return s;
+  if (kda_status s = check_stride("out", desc->out_token_stride, HD, HD, &os)) return s;
+  if (T > 0) {
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(out))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "q/k/v/g/out must be 16-byte aligned");
+    if ((qs | ks | vs | gs | os) & 7)
+      return fail(KDA_ERR_INVALID_ARGUMENT, "q/k/v/g/out token strides must be multiples of 8");
+    const Span so = span_of(out, T, os, HD, 2);
+    const void* ins[4] = {q, k, v, g};
+    const int64_t sts[4] = {qs, ks, vs, gs};
+    for (int i = 0; i < 4; ++i)
+      if (overlaps(so, span_of(ins[i], T, sts[i], HD, 2)))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "out overlaps an input");
+    if (overlaps(so, span_of(beta_logits, T, bs, H, 2)))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "out overlaps beta_logits");
+  }
+  if ((initial_state && !aligned16(initial_state)) || (final_state && !aligned16(final_state)))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "state buffers must be 16-byte aligned");
+  const size_t need = kda_chunk_prefill_workspace_size(N, T, H, KDA_HEAD_DIM);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need,
+                workspace ? workspace_bytes : static_cast<size_t>(0));
+  if (need > 0 && !aligned16(workspace))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  if (N == 0) return ok();
+
+  kda::PrefillParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.g = static_cast<const uint16_t*>(g);
+  p.beta = static_cast<const uint16_t*>(beta_logits);
+  p.A_log = A_log;
+  p.dt_bias = dt_bias;
+  p.cu = cu_seqlens;
+  p.init = initial_state;
+  p.init_idx = initial_state_idx;
+  p.out = static_cast<uint16_t*>(out);
+  p.final_state = final_state;
+  p.work = static_cast<unsigned char*>(workspace);
+  p.lb_log2e = lower_bound * kda::LOG2E;
+  p.scale = desc->scale > 0.f ? desc->scale : 1.0f / std::sqrt(static_cast<float>(KDA_HEAD_DIM));
+  p.N = N;
+  p.T_total = T;
+  p.H = H;
+  p.num_slots_chunk = static_cast<int>(kda::chunk_slots(N, T));
+  p.init_rows = desc->num_state_rows;
+  p.q_st = qs; p.k_st = ks; p.v_st = vs; p.g_st = gs; p.b_st = bs; p.o_st = os;
+  const hipError_t e = kda::launch_prefill(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+kda_status kda_recurrent_verify(const void* q, const void* k, const void* v, const void* g,
+                                const void* beta_logits, const float* A_log, const float* dt_bias,
+                                float lower_bound, const float* state_pool,
+                                const int32_t* state_idx, float* intermediate_state, void* out,
+                                const kda_verify_desc* desc, void* stream) {
+  if (!desc) return fail(KDA_ERR_INVALID_ARGUMENT, "desc is NULL");
+  const int B = desc->batch, T = desc->num_steps, H = desc->num_heads;
+  if (desc->head_dim != KDA_HEAD_DIM)
+    return fail(KDA_ERR_UNSUPPORTED, "head_dim %d unsupported (only 128)", desc->head_dim);
+  if (B < 0 || H < 1 || desc->num_slots < 1)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "bad sizes B=%d H=%d slots=%d", B, H, desc->num_slots);
+  if (T < 1 || T > KDA_MAX_VERIFY_STEPS)
+    return fail(KDA_ERR_UNSUPPORTED, "num_steps %d outside 1..%d", T, KDA_MAX_VERIFY_STEPS);
+  if (kda_status s = check_lower_bound(lower_bound)) return s;
+  if (!A_log || !dt_bias || !state_pool)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "A_log / dt_bias / state_pool is NULL");
+  if (B > 0 && (!q || !k || !v || !g || !beta_logits || !state_idx || !intermediate_state || !out))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "an input or output pointer is NULL");
+  const int64_t HD = static_cast<int64_t>(H) * KDA_HEAD_DIM;
+  int64_t qs, ks, vs, gs, bs, os;
+  if (kda_status s = check_stride("q", desc->q_token_stride, HD, HD, &qs)) return s;
+  if (kda_status s = check_stride("k", desc->k_token_stride, HD, HD, &ks)) return s;
+  if (kda_status s = check_stride("v", desc->v_token_stride, HD, HD, &vs)) return s;
+  if (kda_status s = check_stride("g", desc->g_token_stride, HD, HD, &gs)) return s;
+  if (kda_status s = check_stride("beta_logits", desc->beta_token_stride, H, H, &bs)) return s;
+  if (kda_status s = check_stride("out", desc->out_token_stride, HD, HD, &os)) return s;
+  if (B == 0) return ok();
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(out) ||
+      !aligned16(state_pool) || !aligned16(intermediate_state) || !aligned16(dt_bias))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "tensors must be 16-byte aligned");
+  if ((qs | ks | vs | gs | os) & 7)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "q/k/v/g/out token strides must be multiples of 8");
+  const int64_t BT = static_cast<int64_t>(B) * T;
+  const int64_t state_elems = static_cast<int64_t>(KDA_HEAD_DIM) * KDA_HEAD_DIM;
+  const Span s_pool = span_of(state_pool, desc->num_slots, H * state_elems, H * state_elems, 4);
+  const Span s_int = span_of(intermediate_state, BT, H * state_elems, H * state_elems, 4);
+  if (overlaps(s_pool, s_int))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "intermediate_state overlaps state_pool");
+  const Span so = span_of(out, BT, os, HD, 2);
+  const void* ins[4] = {q, k, v, g};
+  const int64_t sts[4] = {qs, ks, vs, gs};
+  for (int i = 0; i < 4; ++i)
+    if (overlaps(so, span_of(ins[i], BT, sts[i], HD, 2)))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "out overlaps an input");
+  if (overlaps(so, s_int) || overlaps(so, s_pool))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "out overlaps a state buffer");
+
+  kda::VerifyParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.g = static_cast<const uint16_t*>(g);
+  p.beta = static_cast<const uint16_t*>(beta_logits);
+  p.A_log = A_log;
+  p.dt_bias = dt_bias;
+  p.pool = state_pool;
+  p.idx = state_idx;
+  p.inter = intermediate_state;
+  p.out = static_cast<uint16_t*>(out);
+  p.lb_log2e = lower_bound * kda::LOG2E;
+  p.scale = desc->scale > 0.f ? desc->scale : 1.0f / std::sqrt(static_cast<float>(KDA_HEAD_DIM));
+  p.B = B;
+  p.T = T;
+  p.H = H;
+  p.slots = desc->num_slots;
+  p.q_st = qs; p.k_st = ks; p.v_st = vs; p.g_st = gs; p.b_st = bs; p.o_st = os;
+  const hipError_t e = kda::launch_verify(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "verify launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

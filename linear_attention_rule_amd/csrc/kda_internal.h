@@ -1,0 +1,96 @@
+// Internal declarations shared by the libkda host code and its HIP kernels.
+// Device helpers here are small bit-level conversions and the fp32 gate /
+// sigmoid / norm pieces every KDA kernel needs (vLLM PR #55737, opening commit
+// message: bounded gate, in-kernel q/k L2 norm, beta from raw logits).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int D = 128;             // head_dim (key and value channels)
+constexpr int CHUNK = 64;          // prefill chunk length (tokens)
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float L2_EPS = 1e-6f;
+constexpr int KDA_MAX_STEPS_INTERNAL = 64;   // == KDA_MAX_VERIFY_STEPS in include/kda.h
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- device helpers
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+__device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// sigmoid(x) = 1 / (1 + 2^(-x log2 e)); saturates to exactly 0 or 1 at the ends.
+__device__ __forceinline__ float sigmoid_f32(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * LOG2E));
+}
+
+// ---------------------------------------------------------------- launch parameters
+struct VerifyParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* g;
+  const uint16_t* beta;
+  const float* A_log;
+  const float* dt_bias;
+  const float* pool;
+  const int32_t* idx;
+  float* inter;
+  uint16_t* out;
+  float lb_log2e;      // lower_bound * log2(e): gate computed in log2 units
+  float scale;
+  int B, T, H, slots;
+  int64_t q_st, k_st, v_st, g_st, b_st, o_st;
+};
+
+struct PrefillParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* g;
+  const uint16_t* beta;
+  const float* A_log;
+  const float* dt_bias;
+  const int32_t* cu;
+  const float* init;
+  const int32_t* init_idx;
+  uint16_t* out;
+  float* final_state;
+  unsigned char* work;  // chunk records
+  float lb_log2e;
+  float scale;
+  int N, T_total, H, num_slots_chunk, init_rows;
+  int64_t q_st, k_st, v_st, g_st, b_st, o_st;
+};
+
+// Chunk record written by the intra-chunk kernel and read by the state-scan kernel.
+// 60 fp16 MFMA fragments of 1 KiB (64 lanes x 8 halves) + Gamma_C (128 fp32) + pad.
+constexpr int REC_FRAGS = 60;
+constexpr int REC_BYTES = 61 * 1024;
+constexpr int FR_KG = 0;    // -(k^ * Gamma), A operand [token x key], (tb, s): 16
+constexpr int FR_TP = 16;   // T' = (I+A)^-1 diag(beta), A operand [token x token]: 6
+constexpr int FR_QG = 22;   // scale * q^ * Gamma, B operand of O^T [key x token]: 16
+constexpr int FR_PM = 38;   // scale * tril(P), B operand of O^T [token x token]: 6
+constexpr int FR_KC = 44;   // K_C^T, A operand [key x token], (cb, s'): 16
+constexpr int REC_GAMMA_OFF = REC_FRAGS * 1024;
+
+inline int64_t chunk_slots(int N, int T_total) { return static_cast<int64_t>(T_total / CHUNK) + N; }
+
+// Launchers (enqueue only; return the hipGetLastError() of the launch).
+hipError_t launch_verify(const VerifyParams& p, hipStream_t s);
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
+
+}  // namespace kda

@@ -1,0 +1,593 @@
+// Varlen chunked KDA prefill for gfx950 (CDNA4): two kernels on the caller's stream.
+//
+// Role: the FlashKDA prefill of vLLM PR #55737 ("Use FlashKDA for KDA chunked
+// prefill"): bounded gate, in-kernel q/k L2 norm and sigmoid of raw beta
+// logits fused in, output written straight into the caller's layer buffer, final
+// state returned.  The chunked form itself is derived from the token recurrence
+// (no page writes it out): inside a chunk of C = 64 tokens with per-channel
+// log-decays a_t, b_t = a_1 + ... + a_t and Gamma_t = 2^(b_t) (log2 units here),
+//     G_ti = sum_c k_tc k_ic Gamma_tc / Gamma_ic   (i < t),  A = diag(beta) G
+//     P_ti = sum_c q_tc k_ic Gamma_tc / Gamma_ic   (i <= t)
+//     T'   = (I + A)^-1 diag(beta)
+//     U    = T' (V - K_Gamma S)                       K_Gamma[t] = k_t * Gamma_t
+//     O    = scale (Q_Gamma S + tril(P) U)            Q_Gamma[t] = q_t * Gamma_t
+//     S'   = Diag(Gamma_C) S + K_C^T U                K_C[t]     = k_t * Gamma_C / Gamma_t
+//
+// Kernel 1 (prefill_intra): one workgroup per (chunk, head), fully parallel.
+//   Computes everything that does not depend on the state: norms, gates, the
+//   in-chunk cumulative decay, G and P on MFMA, the unit-lower-triangular
+//   inverse, and writes a 61 KiB record of fp16 MFMA fragments (-K_Gamma, T',
+//   scale*Q_Gamma, scale*tril(P), K_C^T) plus Gamma_C.  Fragments are stored
+//   in exactly the per-lane order kernel 2 feeds to v_mfma_f32_16x16x32_f16,
+//   so kernel 2 copies each record linearly into LDS.
+//   Exponent range: Gamma_t itself underflows over a 64-token chunk, so G and P
+//   are formed per 16-token row block m with the block's start as reference:
+//   left factor 2^(b_t - base_m) <= 1 and right factor 2^(base_m - b_i), which
+//   is <= 1 off the diagonal and <= 2^(16*5*log2 e) < 2^116 on it -- inside the
+//   bf16/fp32 exponent range for lower_bound >= -5.  G uses bf16 operands; P
+//   uses a three-product bf16 split (hi*hi + hi*lo + lo*hi), since its rounding
+//   reaches the output directly.
+// Kernel 2 (prefill_scan): one workgroup per (sequence, head, value slice),
+//   sequential over the sequence's chunks.  Each wave owns 16 value columns;
+//   the [128 x 16] fp32 state lives in registers in the MFMA accumulator layout.
+//   That layout is reused as the next product's operand by pairing 16-row
+//   blocks (2s, 2s+1) into one 32-deep k-step, so no shuffles are needed; the
+//   record fragments carry the matching k order.  Records are double-buffered
+//   in LDS with global_load_lds_dwordx4 so the next chunk's copy overlaps the
+//   current chunk's MFMAs.
+#include "kda_internal.h"
+
+namespace kda {
+
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Key/value channel held by lane group g in element e of k-step s (pairs of
+// 16-row accumulator blocks 2s and 2s+1 form one 32-deep k-step).
+__device__ __forceinline__ constexpr int kperm(int s, int g, int e) {
+  return 32 * s + 16 * (e >> 2) + 4 * g + (e & 3);
+}
+
+__device__ __forceinline__ f32x4 mfma_f16(half8 a, half8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Inclusive prefix sum over the 16 lanes of each DPP row.
+__device__ __forceinline__ float row_scan16(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, true));
+  return x;
+}
+
+__device__ __forceinline__ void load4_bf16(const uint16_t* p, float* dst) {
+  const uint2 w = *reinterpret_cast<const uint2*>(p);
+  dst[0] = bf16lo_to_f32(w.x);
+  dst[1] = bf16hi_to_f32(w.x);
+  dst[2] = bf16lo_to_f32(w.y);
+  dst[3] = bf16hi_to_f32(w.y);
+}
+
+// ============================================================================
+// Kernel 1: intra-chunk work, one workgroup (4 waves) per (chunk slot, head).
+// Thread (w, l): token t = 16w + l%16 of the chunk, key channels kperm(s, l/16, e)
+// for s = 0..3, e = 0..7 (32 channels).
+// ============================================================================
+
+constexpr int ATS = 68;   // padded row stride (floats) of the 64x64 LDS matrices
+constexpr int KCS = 72;   // padded row stride (halves) of the transposed K_C tile
+
+struct IntraSmem {
+  float AT[64 * ATS];          // A = diag(beta) strict(G), inverted in place into T
+  float P[64 * ATS];           // scale * tril(P)
+  union {
+    float R0[3 * 4 * 64 * 8];  // right factors of row blocks 0..2 (fp32), by (block, s, lane, e)
+    struct {
+      _Float16 KCt[128 * KCS]; // K_C transposed [channel][token]
+      float tmp[3][256];       // 16x16 partial products of the block inverse
+    } late;
+  } u;
+  float tot[4][128];           // per-block sums of log2 decay
+  float Eb[5][128];            // 2^(base_m), m = 0..4 (base_4 = chunk total)
+  float KCb[4][128];           // 2^(total - base_m)
+  float Dsc[6][128];           // 2^(base_m - base_w), m > w, pair index m*(m-1)/2 + w
+  float beta[64];
+};
+
+__device__ __forceinline__ int pair_idx(int m, int w) { return m * (m - 1) / 2 + w; }
+
+// C = X * Y for 16x16 fp32 blocks in LDS (row strides ldx, ldy), accumulated into acc.
+__device__ __forceinline__ f32x4 mm16_lds(const float* X, int ldx, const float* Y, int ldy,
+                                          f32x4 acc, int lane) {
+  const int r = lane & 15, k = lane >> 4;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    acc = mfma_f32(X[r * ldx + 4 * kk + k], Y[(4 * kk + k) * ldy + r], acc);
+  return acc;
+}
+
+// Store a 16x16 accumulator tile (lane (n, g) holds rows 4g..4g+3 of column n).
+__device__ __forceinline__ void store_tile(float* dst, int ld, f32x4 c, int lane, float mul) {
+  const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) dst[(4 * g + r) * ld + n] = mul * c[r];
+}
+
+__global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) {
+  __shared__ IntraSmem sm;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, m = lane & 15, g = lane >> 4;
+  const int slot = blockIdx.x, h = blockIdx.y, H = p.H;
+
+  // ---- a0: chunk map.  Sequence n owns slots [cu[n]/64 + n, ... + nchunks); find the
+  // last n whose first slot is <= this one (binary search on device, no host sync).
+  int lo = 0, hi = p.N - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.cu[mid] / CHUNK + mid <= slot) lo = mid; else hi = mid - 1;
+  }
+  const int n = lo;
+  const int cs = p.cu[n], ce = p.cu[n + 1];
+  const int jc = slot - (cs / CHUNK + n);
+  if (jc * CHUNK >= ce - cs) return;                     // surplus slot (uniform exit)
+  const int t0 = cs + jc * CHUNK;
+  const int L = min(CHUNK, ce - t0);
+  unsigned char* rec = p.work + (static_cast<int64_t>(slot) * H + h) * REC_BYTES;
+
+  // ---- a1: loads, norms, gate, beta.
+  const int t = 16 * w + m;
+  const bool valid = t < L;
+  const int64_t tok = static_cast<int64_t>(t0) + t;
+  float qv[32], kv[32], la[32];
+  {
+    float gv[32];
+    if (valid) {
+      const uint16_t* qp = p.q + tok * p.q_st + h * D;
+      const uint16_t* kp = p.k + tok * p.k_st + h * D;
+      const uint16_t* gp = p.g + tok * p.g_st + h * D;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int c0 = kperm(s, g, 4 * hh);
+          load4_bf16(qp + c0, qv + 8 * s + 4 * hh);
+          load4_bf16(kp + c0, kv + 8 * s + 4 * hh);
+          load4_bf16(gp + c0, gv + 8 * s + 4 * hh);
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) qv[i] = kv[i] = gv[i] = 0.f;
+    }
+    const float eA = __builtin_amdgcn_exp2f(p.A_log[h] * LOG2E);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const float4 dt = *reinterpret_cast<const float4*>(p.dt_bias + h * D + kperm(s, g, 4 * hh));
+        const float d4[4] = {dt.x, dt.y, dt.z, dt.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 8 * s + 4 * hh + e;
+          la[i] = valid ? p.lb_log2e * sigmoid_f32(eA * (gv[i] + d4[e])) : 0.f;
+        }
+      }
+  }
+  float ssq = 0.f, ssk = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    ssq += qv[i] * qv[i];
+    ssk += kv[i] * kv[i];
+  }
+  ssq += __shfl_xor(ssq, 16);
+  ssq += __shfl_xor(ssq, 32);
+  ssk += __shfl_xor(ssk, 16);
+  ssk += __shfl_xor(ssk, 32);
+  const float rq = __builtin_amdgcn_rsqf(ssq + L2_EPS);
+  const float rk = __builtin_amdgcn_rsqf(ssk + L2_EPS);
+  if (g == 0)
+    sm.beta[t] = valid ? sigmoid_f32(bf16_to_f32(p.beta[tok * p.b_st + h])) : 0.f;
+
+  // In-block inclusive cumulative log2 decay (lanes m = 0..15 of a row are 16 tokens).
+#pragma unroll
+  for (int i = 0; i < 32; ++i) la[i] = row_scan16(la[i]);
+  if (m == 15) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sm.tot[w][kperm(s, g, e)] = la[8 * s + e];
+  }
+  __syncthreads();
+
+  // Per-channel tables from the four block sums (2 threads per channel).
+  {
+    const int c = tid & 127, part = tid >> 7;
+    float base[5];
+    base[0] = 0.f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) base[b + 1] = base[b] + sm.tot[b][c];
+    if (part == 0) {
+#pragma unroll
+      for (int b = 0; b < 5; ++b) sm.Eb[b][c] = __builtin_amdgcn_exp2f(base[b]);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) sm.KCb[b][c] = __builtin_amdgcn_exp2f(base[4] - base[b]);
+    } else {
+#pragma unroll
+      for (int mm = 1; mm < 4; ++mm)
+#pragma unroll
+        for (int ww = 0; ww < mm; ++ww)
+          sm.Dsc[pair_idx(mm, ww)][c] = __builtin_amdgcn_exp2f(base[mm] - base[ww]);
+    }
+  }
+  __syncthreads();
+  if (tid < 128) reinterpret_cast<float*>(rec + REC_GAMMA_OFF)[tid] = sm.Eb[4][tid];
+
+  // ---- operands.  b = la (in-block cumulative), Lf = 2^b <= 1, Rf = 2^-b >= 1.
+  bf16x8 KL[4], QLh[4], QLl[4], Rh[4], Rl[4];
+  _Float16 kch[32];
+  {
+    const float rqs = rq * p.scale;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      half8 kg, qg;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = 8 * s + e;
+        const int c = kperm(s, g, e);
+        const float Lf = __builtin_amdgcn_exp2f(la[i]);
+        const float Rf = __builtin_amdgcn_exp2f(-la[i]);
+        const float kh = kv[i] * rk;
+        const float qh = qv[i] * rq;
+        const float gam = sm.Eb[w][c] * Lf;
+        kg[e] = static_cast<_Float16>(-kh * gam);
+        qg[e] = static_cast<_Float16>(qv[i] * rqs * gam);
+        kch[i] = static_cast<_Float16>(sm.KCb[w][c] * Rf * kh);
+        KL[s][e] = static_cast<__bf16>(kh * Lf);
+        const float ql = qh * Lf;
+        const __bf16 qlh = static_cast<__bf16>(ql);
+        QLh[s][e] = qlh;
+        QLl[s][e] = static_cast<__bf16>(ql - static_cast<float>(qlh));
+        const float r0 = kh * Rf;
+        const __bf16 r0h = static_cast<__bf16>(r0);
+        Rh[s][e] = r0h;
+        Rl[s][e] = static_cast<__bf16>(r0 - static_cast<float>(r0h));
+        kv[i] = r0;  // keep the fp32 right factor for publication
+      }
+      *reinterpret_cast<half8*>(rec + (FR_KG + 4 * w + s) * 1024 + lane * 16) = kg;
+      *reinterpret_cast<half8*>(rec + (FR_QG + 4 * w + s) * 1024 + lane * 16) = qg;
+    }
+  }
+  if (w < 3) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      float* dst = sm.u.R0 + ((w * 4 + s) * 64 + lane) * 8;
+      *reinterpret_cast<float4*>(dst) = make_float4(kv[8 * s], kv[8 * s + 1], kv[8 * s + 2], kv[8 * s + 3]);
+      *reinterpret_cast<float4*>(dst + 4) =
+          make_float4(kv[8 * s + 4], kv[8 * s + 5], kv[8 * s + 6], kv[8 * s + 7]);
+    }
+  }
+  __syncthreads();
+
+  // ---- a2: G and P for row block w, column blocks 0..w (MFMA).
+  for (int wb = 0; wb <= w; ++wb) {
+    f32x4 accG = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8 bh, bl;
+      if (wb == w) {
+        bh = Rh[s];
+        bl = Rl[s];
+      } else {
+        const float* src = sm.u.R0 + ((wb * 4 + s) * 64 + lane) * 8;
+        const float* dsc = sm.Dsc[pair_idx(w, wb)];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float r = src[e] * dsc[kperm(s, g, e)];
+          const __bf16 rh = static_cast<__bf16>(r);
+          bh[e] = rh;
+          bl[e] = static_cast<__bf16>(r - static_cast<float>(rh));
+        }
+      }
+      accG = mfma_bf16(KL[s], bh, accG);
+      accP = mfma_bf16(QLh[s], bh, accP);
+      accP = mfma_bf16(QLh[s], bl, accP);
+      accP = mfma_bf16(QLl[s], bh, accP);
+    }
+    // lane (n, g) holds rows t = 16w + 4g + r, column i = 16wb + n
+    const int i = 16 * wb + m;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tr = 16 * w + 4 * g + r;
+      sm.AT[tr * ATS + i] = (i < tr) ? sm.beta[tr] * accG[r] : 0.f;
+      sm.P[tr * ATS + i] = (i <= tr) ? p.scale * accP[r] : 0.f;
+    }
+  }
+  for (int wb = w + 1; wb < 4; ++wb) {
+    const int i = 16 * wb + m;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tr = 16 * w + 4 * g + r;
+      sm.AT[tr * ATS + i] = 0.f;
+      sm.P[tr * ATS + i] = 0.f;
+    }
+  }
+  __syncthreads();   // R0 is dead from here on; the union's late view may be written
+
+  // K_C transposed into LDS ([channel][token]) for the K_C^T fragments.
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sm.u.late.KCt[kperm(s, g, e) * KCS + t] = kch[8 * s + e];
+
+  // ---- a3: T = (I + A)^-1.  Diagonal 16x16 blocks by forward substitution (one
+  // column per lane, the four lane groups redundant), in place.
+  {
+    const int j = m;
+    float x[16];
+    const float* Ab = sm.AT + (16 * w) * ATS + 16 * w;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float acc = (r == j) ? 1.f : 0.f;
+#pragma unroll
+      for (int c = 0; c < r; ++c) acc -= Ab[r * ATS + c] * x[c];
+      x[r] = acc;
+    }
+    // All lanes of this wave have read block (w, w) before any lane writes it.
+    __builtin_amdgcn_wave_barrier();
+    if (g == 0) {
+      float* Tb = sm.AT + (16 * w) * ATS + 16 * w;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Tb[r * ATS + j] = x[r];
+    }
+  }
+  __syncthreads();
+  // Off-diagonal blocks row by row: T_rc = -T_rr * sum_{j=c}^{r-1} A_rj T_jc, computed in
+  // place (A_rc is last needed by T_rc itself; all reads of a row precede its writes).
+  for (int rb = 1; rb < 4; ++rb) {
+    const int cb = w;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (cb < rb) {
+      for (int jb = cb; jb < rb; ++jb)
+        acc = mm16_lds(sm.AT + (16 * rb) * ATS + 16 * jb, ATS, sm.AT + (16 * jb) * ATS + 16 * cb,
+                       ATS, acc, lane);
+      store_tile(sm.u.late.tmp[cb], 16, acc, lane, 1.f);
+    }
+    __syncthreads();
+    if (cb < rb) {
+      f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      z = mm16_lds(sm.AT + (16 * rb) * ATS + 16 * rb, ATS, sm.u.late.tmp[cb], 16, z, lane);
+      store_tile(sm.AT + (16 * rb) * ATS + 16 * cb, ATS, z, lane, -1.f);
+    }
+    __syncthreads();
+  }
+
+  // ---- record fragments: T' = T diag(beta) and scale*tril(P) (row-major in LDS), K_C^T.
+  // A/B fragment (row block rb, k-step s'): lane (r, g) holds row 16rb + r, columns
+  // kperm(s', g, 0..7).
+  {
+    const int rb = w;
+    for (int sp = 0; sp <= (rb >> 1); ++sp) {
+      const int fi = (rb < 2) ? rb : 2 + 2 * (rb - 2) + sp;
+      const int row = 16 * rb + m;
+      const int c0 = kperm(sp, g, 0), c1 = kperm(sp, g, 4);
+      const float4 ta = *reinterpret_cast<const float4*>(sm.AT + row * ATS + c0);
+      const float4 tb = *reinterpret_cast<const float4*>(sm.AT + row * ATS + c1);
+      const float4 ba = *reinterpret_cast<const float4*>(sm.beta + c0);
+      const float4 bb = *reinterpret_cast<const float4*>(sm.beta + c1);
+      half8 tf = {static_cast<_Float16>(ta.x * ba.x), static_cast<_Float16>(ta.y * ba.y),
+                  static_cast<_Float16>(ta.z * ba.z), static_cast<_Float16>(ta.w * ba.w),
+                  static_cast<_Float16>(tb.x * bb.x), static_cast<_Float16>(tb.y * bb.y),
+                  static_cast<_Float16>(tb.z * bb.z), static_cast<_Float16>(tb.w * bb.w)};
+      *reinterpret_cast<half8*>(rec + (FR_TP + fi) * 1024 + lane * 16) = tf;
+      const float4 pa = *reinterpret_cast<const float4*>(sm.P + row * ATS + c0);
+      const float4 pb = *reinterpret_cast<const float4*>(sm.P + row * ATS + c1);
+      half8 pf = {static_cast<_Float16>(pa.x), static_cast<_Float16>(pa.y),
+                  static_cast<_Float16>(pa.z), static_cast<_Float16>(pa.w),
+                  static_cast<_Float16>(pb.x), static_cast<_Float16>(pb.y),
+                  static_cast<_Float16>(pb.z), static_cast<_Float16>(pb.w)};
+      *reinterpret_cast<half8*>(rec + (FR_PM + fi) * 1024 + lane * 16) = pf;
+    }
+    // K_C^T fragments (channel block cb, token k-step s'): lane (r, g) holds channel
+    // 16cb + r, tokens kperm(s', g, 0..7).
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2) {
+      const int cb = 2 * w + q2;
+#pragma unroll
+      for (int sp = 0; sp < 2; ++sp) {
+        const _Float16* src = sm.u.late.KCt + (16 * cb + m) * KCS;
+        const uint2 a = *reinterpret_cast<const uint2*>(src + kperm(sp, g, 0));
+        const uint2 b = *reinterpret_cast<const uint2*>(src + kperm(sp, g, 4));
+        *reinterpret_cast<uint4*>(rec + (FR_KC + 2 * cb + sp) * 1024 + lane * 16) =
+            make_uint4(a.x, a.y, b.x, b.y);
+      }
+    }
+  }
+}
+
+// ============================================================================
+// Kernel 2: state scan, one workgroup of NW waves per (sequence, head, value slice).
+// ============================================================================
+
+__device__ __forceinline__ void copy_record_async(const unsigned char* src, unsigned char* dst,
+                                                  int wave, int nw, int lane) {
+  for (int f = wave; f < REC_BYTES / 1024; f += nw)
+    __builtin_amdgcn_global_load_lds(
+        reinterpret_cast<const void*>(src + f * 1024 + lane * 16),
+        (__attribute__((address_space(3))) void*)(dst + f * 1024), 16, 0, 0);
+}
+
+__device__ __forceinline__ half8 frag(const unsigned char* r, int f, int lane) {
+  return *reinterpret_cast<const half8*>(r + f * 1024 + lane * 16);
+}
+
+__device__ __forceinline__ half8 pack_f16(f32x4 a, f32x4 b) {
+  half8 h = {static_cast<_Float16>(a[0]), static_cast<_Float16>(a[1]),
+             static_cast<_Float16>(a[2]), static_cast<_Float16>(a[3]),
+             static_cast<_Float16>(b[0]), static_cast<_Float16>(b[1]),
+             static_cast<_Float16>(b[2]), static_cast<_Float16>(b[3])};
+  return h;
+}
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void prefill_scan_kernel(PrefillParams p) {
+  __shared__ __attribute__((aligned(16))) unsigned char srec[2][REC_BYTES];
+  constexpr int BV = 16 * NW;
+  constexpr int NVS = D / BV;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, nl = lane & 15, g = lane >> 4;
+  int blk = blockIdx.x;
+  const int vs = blk % NVS;
+  blk /= NVS;
+  const int h = blk % p.H;
+  const int n = blk / p.H;
+  const int H = p.H;
+  const int v0 = vs * BV + 16 * w;     // this wave's 16 value columns
+  const int cs = p.cu[n], ce = p.cu[n + 1];
+  const int len = ce - cs;
+  const int nch = (len + CHUNK - 1) / CHUNK;
+  const int64_t slot0 = cs / CHUNK + n;
+  const int64_t HDD = static_cast<int64_t>(D) * D;
+
+  // Start state: S[cb][r] = S[16cb + 4g + r][v0 + nl].
+  f32x4 S[8];
+  {
+    int row = -1;
+    if (p.init) {
+      if (p.init_idx) {
+        const int ri = p.init_idx[n];
+        row = (ri >= 0 && ri < p.init_rows) ? ri : -1;
+      } else {
+        row = n;
+      }
+    }
+    if (row >= 0) {
+      const float* src = p.init + (static_cast<int64_t>(row) * H + h) * HDD + v0 + nl;
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[cb][r] = src[(16 * cb + 4 * g + r) * D];
+    } else {
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb) S[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+
+  const unsigned char* recbase = p.work + (slot0 * H + h) * REC_BYTES;
+  const int64_t rec_stride = static_cast<int64_t>(H) * REC_BYTES;
+  if (nch > 0) copy_record_async(recbase, srec[0], w, NW, lane);
+
+  for (int j = 0; j < nch; ++j) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (j + 1 < nch) copy_record_async(recbase + (j + 1) * rec_stride, srec[(j + 1) & 1], w, NW, lane);
+    const unsigned char* R = srec[j & 1];
+    const int tb0 = cs + j * CHUNK;
+    const int Lc = min(CHUNK, ce - tb0);
+
+    half8 Sf[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) Sf[s] = pack_f16(S[2 * s], S[2 * s + 1]);
+
+    // X = V - K_Gamma S   (rows = tokens, lane column = value channel)
+    f32x4 X[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tt = 16 * tb + 4 * g + r;
+        X[tb][r] = (tt < Lc)
+                       ? bf16_to_f32(p.v[static_cast<int64_t>(tb0 + tt) * p.v_st + h * D + v0 + nl])
+                       : 0.f;
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) X[tb] = mfma_f16(frag(R, FR_KG + 4 * tb + s, lane), Sf[s], X[tb]);
+    }
+    // U = T' X
+    const half8 Xf0 = pack_f16(X[0], X[1]), Xf1 = pack_f16(X[2], X[3]);
+    f32x4 U[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) U[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    U[0] = mfma_f16(frag(R, FR_TP + 0, lane), Xf0, U[0]);
+    U[1] = mfma_f16(frag(R, FR_TP + 1, lane), Xf0, U[1]);
+    U[2] = mfma_f16(frag(R, FR_TP + 2, lane), Xf0, U[2]);
+    U[2] = mfma_f16(frag(R, FR_TP + 3, lane), Xf1, U[2]);
+    U[3] = mfma_f16(frag(R, FR_TP + 4, lane), Xf0, U[3]);
+    U[3] = mfma_f16(frag(R, FR_TP + 5, lane), Xf1, U[3]);
+    const half8 Uf0 = pack_f16(U[0], U[1]), Uf1 = pack_f16(U[2], U[3]);
+
+    // O^T = S^T (scale Q_Gamma)^T + U^T (scale tril P)^T; lane (token, g) holds 4 value columns.
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) o = mfma_f16(Sf[s], frag(R, FR_QG + 4 * tb + s, lane), o);
+      const int fi = (tb < 2) ? tb : 2 + 2 * (tb - 2);
+      o = mfma_f16(Uf0, frag(R, FR_PM + fi, lane), o);
+      if (tb >= 2) o = mfma_f16(Uf1, frag(R, FR_PM + fi + 1, lane), o);
+      const int tt = 16 * tb + nl;
+      if (tt < Lc) {
+        const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16(o[0])) |
+                            (static_cast<uint32_t>(f32_to_bf16(o[1])) << 16);
+        const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16(o[2])) |
+                            (static_cast<uint32_t>(f32_to_bf16(o[3])) << 16);
+        *reinterpret_cast<uint2*>(p.out + static_cast<int64_t>(tb0 + tt) * p.o_st + h * D + v0 +
+                                  4 * g) = make_uint2(w0, w1);
+      }
+    }
+    // S <- Diag(Gamma_C) S + K_C^T U
+    const float* gam = reinterpret_cast<const float*>(R + REC_GAMMA_OFF);
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) {
+      const float4 gc = *reinterpret_cast<const float4*>(gam + 16 * cb + 4 * g);
+      S[cb][0] *= gc.x;
+      S[cb][1] *= gc.y;
+      S[cb][2] *= gc.z;
+      S[cb][3] *= gc.w;
+      S[cb] = mfma_f16(frag(R, FR_KC + 2 * cb + 0, lane), Uf0, S[cb]);
+      S[cb] = mfma_f16(frag(R, FR_KC + 2 * cb + 1, lane), Uf1, S[cb]);
+    }
+  }
+
+  if (p.final_state) {
+    float* dst = p.final_state + (static_cast<int64_t>(n) * H + h) * HDD + v0 + nl;
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[(16 * cb + 4 * g + r) * D] = S[cb][r];
+  }
+}
+
+template <int NW>
+hipError_t launch_scan(const PrefillParams& p, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(p.N) * p.H * (D / (16 * NW)));
+  hipLaunchKernelGGL(prefill_scan_kernel<NW>, grid, dim3(64 * NW), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t s) {
+  if (p.N == 0) return hipSuccess;
+  if (p.num_slots_chunk > 0 && p.T_total > 0) {
+    const dim3 grid(static_cast<unsigned>(p.num_slots_chunk), static_cast<unsigned>(p.H));
+    hipLaunchKernelGGL(prefill_intra_kernel, grid, dim3(256), 0, s, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // Value-slice width per workgroup: enough workgroups to cover the 256 compute
+  // units (one resident workgroup per CU: the double-buffered records use 122 KiB of LDS).
+  const int64_t pairs = static_cast<int64_t>(p.N) * p.H;
+  if (pairs * 2 >= 256) return launch_scan<4>(p, s);
+  if (pairs * 4 >= 256) return launch_scan<2>(p, s);
+  return launch_scan<1>(p, s);
+}
+
+}  // namespace kda

@@ -1,0 +1,205 @@
+// Fused multi-step KDA verify for gfx950.
+//
+// Role: the one-launch verify of TensorRT-LLM PR #21179 ("GLM-5.3-Flash FP8
+// performance fixes on Hopper", fused-verify commit message): every draft step
+// of a row runs in one call, the state starts from the read-only pool and the
+// state after each step is written to its own row of the intermediate buffer.
+//
+// Work split: one workgroup of 256 threads per (row b, head h, value tile).
+// The [128 x BV] fp32 state tile stays in registers for all T steps; thread
+// (rg, cl) owns rows rg*R .. rg*R+R-1 and value columns 4cl .. 4cl+3, so every
+// store of a state row segment is a contiguous BV*4-byte run and a wave writes
+// whole 128-byte lines.  Per step the two key-direction reductions
+// r = S^T k^ and y = S^T q^ share one pass over the decayed state; the output
+// then needs no second pass: o = scale * (y + (k^ . q^) u) with
+// u = beta (v - r), because the update adds k^ u^T.
+//
+// The kernel is bound by the fp32 state writes (T x 64 KiB per (b, h)), so
+// they use non-temporal stores: nothing reads them back in this call.
+#include "kda_internal.h"
+
+namespace kda {
+
+namespace {
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+template <int BV>
+__global__ __launch_bounds__(256) void verify_kernel(VerifyParams p) {
+  constexpr int NCG = BV / 4;      // column groups (float4) per state row
+  constexpr int NRG = 256 / NCG;   // row groups
+  constexpr int R = D / NRG;       // rows per thread
+  constexpr int NVT = D / BV;      // value tiles per head
+  static_assert(R >= 1 && D % NRG == 0, "bad tile");
+
+  extern __shared__ float smem[];
+  const int T = p.T;
+  float* s_alpha = smem;              // [T][128]
+  float* s_khat = s_alpha + T * D;    // [T][128]
+  float* s_qhat = s_khat + T * D;     // [T][128]
+  float* s_v = s_qhat + T * D;        // [T][BV]
+  float* s_beta = s_v + T * BV;       // [T]
+  float* s_kq = s_beta + T;           // [T]
+  float* s_part = s_kq + T;           // [2 parity][4 waves][2 (r, y)][BV]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  int blk = blockIdx.x;
+  const int vt = blk % NVT;
+  blk /= NVT;
+  const int h = blk % p.H;
+  const int b = blk / p.H;
+  const int v0 = vt * BV;
+
+  const int slot = p.idx[b];
+  if (slot < 0 || slot >= p.slots) {
+    // Padding row: zero outputs, no state rows written.
+    for (int e = tid; e < T * BV; e += 256) {
+      const int t = e / BV, c = e % BV;
+      p.out[static_cast<int64_t>(b * T + t) * p.o_st + h * D + v0 + c] = 0;
+    }
+    return;
+  }
+
+  // ---------------- prologue: per-token norms, gates and beta into LDS.
+  const float eA = __builtin_amdgcn_exp2f(p.A_log[h] * LOG2E);
+  const float2 dtb = *reinterpret_cast<const float2*>(p.dt_bias + h * D + 2 * lane);
+  for (int t = wave; t < T; t += 4) {
+    const int64_t tok = static_cast<int64_t>(b) * T + t;
+    const uint32_t qw = *reinterpret_cast<const uint32_t*>(p.q + tok * p.q_st + h * D + 2 * lane);
+    const uint32_t kw = *reinterpret_cast<const uint32_t*>(p.k + tok * p.k_st + h * D + 2 * lane);
+    const uint32_t gw = *reinterpret_cast<const uint32_t*>(p.g + tok * p.g_st + h * D + 2 * lane);
+    const float q0 = bf16lo_to_f32(qw), q1 = bf16hi_to_f32(qw);
+    const float k0 = bf16lo_to_f32(kw), k1 = bf16hi_to_f32(kw);
+    const float g0 = bf16lo_to_f32(gw), g1 = bf16hi_to_f32(gw);
+    const float ssq = wave_sum(q0 * q0 + q1 * q1);
+    const float ssk = wave_sum(k0 * k0 + k1 * k1);
+    const float sqk = wave_sum(q0 * k0 + q1 * k1);
+    const float rq = __builtin_amdgcn_rsqf(ssq + L2_EPS);
+    const float rk = __builtin_amdgcn_rsqf(ssk + L2_EPS);
+    const float a0 = __builtin_amdgcn_exp2f(p.lb_log2e * sigmoid_f32(eA * (g0 + dtb.x)));
+    const float a1 = __builtin_amdgcn_exp2f(p.lb_log2e * sigmoid_f32(eA * (g1 + dtb.y)));
+    *reinterpret_cast<float2*>(s_alpha + t * D + 2 * lane) = make_float2(a0, a1);
+    *reinterpret_cast<float2*>(s_khat + t * D + 2 * lane) = make_float2(k0 * rk, k1 * rk);
+    *reinterpret_cast<float2*>(s_qhat + t * D + 2 * lane) = make_float2(q0 * rq, q1 * rq);
+    if (2 * lane < BV) {
+      const uint32_t vw =
+          *reinterpret_cast<const uint32_t*>(p.v + tok * p.v_st + h * D + v0 + 2 * lane);
+      s_v[t * BV + 2 * lane] = bf16lo_to_f32(vw);
+      s_v[t * BV + 2 * lane + 1] = bf16hi_to_f32(vw);
+    }
+    if (lane == 0) {
+      s_beta[t] = sigmoid_f32(bf16_to_f32(p.beta[tok * p.b_st + h]));
+      s_kq[t] = sqk * rq * rk;
+    }
+  }
+
+  // ---------------- gather the start state from the pool.
+  const int cl = tid % NCG;
+  const int rg = tid / NCG;
+  const int row0 = rg * R;
+  const int64_t head_elems = static_cast<int64_t>(D) * D;
+  float4 S[R];
+  {
+    const float* src = p.pool + (static_cast<int64_t>(slot) * p.H + h) * head_elems +
+                       static_cast<int64_t>(row0) * D + v0 + 4 * cl;
+#pragma unroll
+    for (int j = 0; j < R; ++j) S[j] = *reinterpret_cast<const float4*>(src + j * D);
+  }
+  __syncthreads();
+
+  // ---------------- the T steps.
+  for (int t = 0; t < T; ++t) {
+    const float* al = s_alpha + t * D + row0;
+    const float* kh = s_khat + t * D + row0;
+    const float* qh = s_qhat + t * D + row0;
+    float4 r = make_float4(0.f, 0.f, 0.f, 0.f), y = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const float a = al[j], kk = kh[j], qq = qh[j];
+      S[j].x *= a; S[j].y *= a; S[j].z *= a; S[j].w *= a;
+      r.x += S[j].x * kk; r.y += S[j].y * kk; r.z += S[j].z * kk; r.w += S[j].w * kk;
+      y.x += S[j].x * qq; y.y += S[j].y * qq; y.z += S[j].z * qq; y.w += S[j].w * qq;
+    }
+#pragma unroll
+    for (int off = NCG; off < 64; off <<= 1) {
+      r.x += __shfl_xor(r.x, off); r.y += __shfl_xor(r.y, off);
+      r.z += __shfl_xor(r.z, off); r.w += __shfl_xor(r.w, off);
+      y.x += __shfl_xor(y.x, off); y.y += __shfl_xor(y.y, off);
+      y.z += __shfl_xor(y.z, off); y.w += __shfl_xor(y.w, off);
+    }
+    float* part = s_part + (t & 1) * (4 * 2 * BV);
+    if (lane < NCG) {
+      *reinterpret_cast<float4*>(part + (wave * 2 + 0) * BV + 4 * cl) = r;
+      *reinterpret_cast<float4*>(part + (wave * 2 + 1) * BV + 4 * cl) = y;
+    }
+    __syncthreads();
+    float4 rr = make_float4(0.f, 0.f, 0.f, 0.f), yy = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float4 a = *reinterpret_cast<const float4*>(part + (w * 2 + 0) * BV + 4 * cl);
+      const float4 c = *reinterpret_cast<const float4*>(part + (w * 2 + 1) * BV + 4 * cl);
+      rr.x += a.x; rr.y += a.y; rr.z += a.z; rr.w += a.w;
+      yy.x += c.x; yy.y += c.y; yy.z += c.z; yy.w += c.w;
+    }
+    const float4 vv = *reinterpret_cast<const float4*>(s_v + t * BV + 4 * cl);
+    const float be = s_beta[t], kq = s_kq[t];
+    float4 u;
+    u.x = be * (vv.x - rr.x); u.y = be * (vv.y - rr.y);
+    u.z = be * (vv.z - rr.z); u.w = be * (vv.w - rr.w);
+
+    float* dst = p.inter +
+                 ((static_cast<int64_t>(b) * T + t) * p.H + h) * head_elems +
+                 static_cast<int64_t>(row0) * D + v0 + 4 * cl;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const float kk = kh[j];
+      S[j].x += kk * u.x; S[j].y += kk * u.y; S[j].z += kk * u.z; S[j].w += kk * u.w;
+      const f32x4 sv = {S[j].x, S[j].y, S[j].z, S[j].w};
+      __builtin_nontemporal_store(sv, reinterpret_cast<f32x4*>(dst + j * D));
+    }
+    if (rg == 0) {
+      const float s = p.scale;
+      const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16(s * (yy.x + kq * u.x))) |
+                          (static_cast<uint32_t>(f32_to_bf16(s * (yy.y + kq * u.y))) << 16);
+      const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16(s * (yy.z + kq * u.z))) |
+                          (static_cast<uint32_t>(f32_to_bf16(s * (yy.w + kq * u.w))) << 16);
+      uint16_t* o = p.out + (static_cast<int64_t>(b) * T + t) * p.o_st + h * D + v0 + 4 * cl;
+      *reinterpret_cast<uint2*>(o) = make_uint2(w0, w1);
+    }
+  }
+}
+
+template <int BV>
+size_t verify_lds_bytes(int T) {
+  return sizeof(float) * (static_cast<size_t>(T) * (3 * D + BV) + 2 * T + 2 * 4 * 2 * BV);
+}
+
+template <int BV>
+hipError_t launch_verify_bv(const VerifyParams& p, hipStream_t s) {
+  const size_t lds = verify_lds_bytes<BV>(p.T);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&verify_kernel<BV>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     static_cast<int>(verify_lds_bytes<BV>(KDA_MAX_STEPS_INTERNAL)));
+  if (e != hipSuccess) return e;
+  const dim3 grid(static_cast<unsigned>(p.B) * p.H * (D / BV));
+  hipLaunchKernelGGL(verify_kernel<BV>, grid, dim3(256), lds, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_verify(const VerifyParams& p, hipStream_t s) {
+  if (p.B == 0) return hipSuccess;
+  // Enough workgroups to cover the 256 compute units: split each head's value
+  // columns four ways when there are few (row, head) pairs.
+  if (static_cast<int64_t>(p.B) * p.H >= 256) return launch_verify_bv<128>(p, s);
+  return launch_verify_bv<32>(p, s);
+}
+
+}  // namespace kda

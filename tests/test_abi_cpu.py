@@ -1,0 +1,111 @@
+"""Host-only checks of libkda: it loads, exports what include/kda.h declares,
+and its host-side validation rejects bad arguments before touching a GPU.
+
+No compute call is made here (no GPU in this process); every call below
+returns from argument validation.
+"""
+
+import ctypes
+
+import pytest
+
+import linear_attention_rule_amd as L
+from linear_attention_rule_amd import _binding as B
+
+KDA_OK, INVALID, UNSUPPORTED, WS_SMALL = 0, 1, 2, 3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return L.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = L.header_entry_points()
+    assert set(names) >= {"kda_chunk_prefill", "kda_recurrent_verify", "kda_last_error",
+                          "kda_abi_version", "kda_chunk_prefill_workspace_size"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_workspace_size(lib):
+    assert lib.kda_abi_version() == 1
+    rec = 61 * 1024
+    # chunk slots = floor(T/64) + N
+    assert lib.kda_chunk_prefill_workspace_size(4, 32768, 16, 128) == (512 + 4) * 16 * rec
+    assert lib.kda_chunk_prefill_workspace_size(1, 100, 2, 128) == (1 + 1) * 2 * rec
+    assert lib.kda_chunk_prefill_workspace_size(1, 100, 2, 64) == 0
+    assert lib.kda_chunk_prefill_workspace_size(0, 0, 1, 128) == 0
+
+
+def _fake(n=1):
+    # Non-null, 16-byte-aligned host addresses.  Validation never dereferences
+    # them; every case below fails before a launch.
+    return ctypes.c_void_p(0x10000 * n)
+
+
+def _prefill(lib, desc, lb=-5.0, ws_bytes=1 << 40, null_q=False, null_desc=False):
+    f = _fake
+    return lib.kda_chunk_prefill(None if null_q else f(1), f(2), f(3), f(4), f(5), f(6), f(7), lb,
+                                 f(8), None, None, f(9), f(10), f(11), ws_bytes,
+                                 None if null_desc else ctypes.byref(desc), None)
+
+
+def _pdesc(N=1, T=64, H=2, D=128):
+    return B.PrefillDesc(N, T, H, D, 0.0, 0, 0, 0, 0, 0, 0, 0)
+
+
+def test_prefill_rejects_bad_arguments(lib):
+    assert _prefill(lib, _pdesc(), null_desc=True) == INVALID
+    assert _prefill(lib, _pdesc(D=64)) == UNSUPPORTED
+    assert b"head_dim" in lib.kda_last_error()
+    assert _prefill(lib, _pdesc(), lb=-6.0) == UNSUPPORTED
+    assert _prefill(lib, _pdesc(), lb=0.5) == UNSUPPORTED
+    assert _prefill(lib, _pdesc(), lb=float("nan")) == UNSUPPORTED
+    assert _prefill(lib, _pdesc(), null_q=True) == INVALID
+    assert _prefill(lib, _pdesc(H=0)) == INVALID
+    assert _prefill(lib, _pdesc(), ws_bytes=100) == WS_SMALL
+    assert b"workspace" in lib.kda_last_error()
+    d = _pdesc()
+    d.q_token_stride = 100          # < H*128
+    assert _prefill(lib, d) == INVALID
+    d = _pdesc()
+    d.q_token_stride = 260          # >= H*128 but not a multiple of 8
+    assert _prefill(lib, d) == INVALID
+
+
+def test_prefill_rejects_out_overlapping_input(lib):
+    d = _pdesc(T=64, H=2)
+    f = _fake
+    st = lib.kda_chunk_prefill(f(1), f(2), f(3), f(4), f(5), f(6), f(7), -5.0, f(8), None, None,
+                               f(1), f(10), f(11), 1 << 40, ctypes.byref(d), None)
+    assert st == INVALID and b"overlap" in lib.kda_last_error()
+
+
+def _vdesc(Bn=2, T=8, H=2, D=128, slots=4):
+    return B.VerifyDesc(Bn, T, H, D, 0.0, slots, 0, 0, 0, 0, 0, 0)
+
+
+def _verify(lib, desc, lb=-5.0, inter=None):
+    f = _fake
+    return lib.kda_recurrent_verify(f(1), f(2), f(3), f(4), f(5), f(6), f(7), lb, f(20), f(9),
+                                    inter if inter is not None else f(40), f(50),
+                                    ctypes.byref(desc), None)
+
+
+def test_verify_rejects_bad_arguments(lib):
+    assert _verify(lib, _vdesc(D=96)) == UNSUPPORTED
+    assert _verify(lib, _vdesc(T=0)) == UNSUPPORTED
+    assert _verify(lib, _vdesc(T=65)) == UNSUPPORTED
+    assert _verify(lib, _vdesc(slots=0)) == INVALID
+    assert _verify(lib, _vdesc(), lb=-7.0) == UNSUPPORTED
+    # intermediate overlapping the pool
+    assert _verify(lib, _vdesc(), inter=_fake(20)) == INVALID
+    assert b"overlap" in lib.kda_last_error()
+
+
+def test_zero_sized_calls_are_ok_without_launch(lib):
+    # N = 0 prefill and B = 0 verify enqueue nothing and succeed.
+    assert _prefill(lib, _pdesc(N=0, T=0), ws_bytes=0) == KDA_OK
+    assert _verify(lib, _vdesc(Bn=0)) == KDA_OK
+    assert lib.kda_last_error() == b""

@@ -1,0 +1,258 @@
+"""GPU parity of the varlen chunked prefill against the fp64 oracle.
+
+All calls go through the C ABI (ctypes binding) on seeded inputs from
+linear_attention_rule_amd.workloads.  Small cases are compared element by
+element in full.  At the full workload sizes the GPU runs the real launch (all
+heads, all sequences) and the oracle recomputes a sample of (sequence, head)
+pairs over their whole length: heads are independent, so each sampled pair is
+an exact sub-problem of the same call.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import tolerances as TOL
+from linear_attention_rule_amd import chunk_prefill, recurrent_verify
+from linear_attention_rule_amd import workloads as W
+from oracle import kda_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(data):
+    return {k: (v.to("cuda") if isinstance(v, torch.Tensor) else v) for k, v in data.items()}
+
+
+def _call(d, **kw):
+    return chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta_logits"], d["A_log"], d["dt_bias"],
+                         d["lower_bound"], d["cu_seqlens"], initial_state=d["initial_state"],
+                         initial_state_idx=d["initial_state_idx"], scale=d["scale"], **kw)
+
+
+def _oracle(data, heads=None, seqs=None):
+    """Oracle on a subset of heads / sequences.  Returns (out [T_sel, h_sel, V], final [n_sel, h_sel, K, V])."""
+    f = W.to_f64
+    cu = data["cu_seqlens"].numpy().astype(np.int64)
+    N = len(cu) - 1
+    H = data["q"].shape[1]
+    heads = list(range(H)) if heads is None else list(heads)
+    seqs = list(range(N)) if seqs is None else list(seqs)
+    rows = np.concatenate([np.arange(cu[n], cu[n + 1]) for n in seqs]) if seqs else np.zeros(0, int)
+    sub_cu = np.concatenate([[0], np.cumsum([cu[n + 1] - cu[n] for n in seqs])]).astype(np.int64)
+    pick = lambda t: f(t)[rows][:, heads]
+    init = data["initial_state"]
+    idx = data["initial_state_idx"]
+    sub_init = None
+    sub_idx = None
+    if init is not None:
+        if idx is None:
+            sub_init = init.numpy()[seqs][:, heads]
+        else:
+            sub_init = init.numpy()[:, heads]
+            sub_idx = idx.numpy()[seqs]
+            # indices outside the pool start from zero
+            bad = (sub_idx < 0) | (sub_idx >= sub_init.shape[0])
+            if bad.any():
+                sub_init = np.concatenate([sub_init, np.zeros((1,) + sub_init.shape[1:])])
+                sub_idx = np.where(bad, sub_init.shape[0] - 1, sub_idx)
+    o, fs = O.chunk_prefill(pick(data["q"]), pick(data["k"]), pick(data["v"]), pick(data["g"]),
+                            f(data["beta_logits"])[rows][:, heads], f(data["A_log"])[heads],
+                            f(data["dt_bias"])[heads], data["lower_bound"], sub_cu, sub_init,
+                            sub_idx, scale=data["scale"])
+    return o, fs, rows
+
+
+def _compare(data, out, final, heads=None, seqs=None):
+    o_ref, f_ref, rows = _oracle(data, heads, seqs)
+    H = data["q"].shape[1]
+    N = data["cu_seqlens"].numel() - 1
+    heads = list(range(H)) if heads is None else list(heads)
+    seqs = list(range(N)) if seqs is None else list(seqs)
+    og = out[torch.as_tensor(rows, device=out.device)][:, heads] if len(rows) else out[:0]
+    e = TOL.assert_output_ok(og, o_ref) if len(rows) else {}
+    r = None
+    if final is not None:
+        fg = final[seqs][:, heads]
+        r = TOL.assert_state_ok(fg, f_ref)
+    print("output errors", e, "state rel", r, flush=True)
+    return e, r
+
+
+def test_prefill_tiny_1x256_h2():
+    case = W.TINY
+    print(f"case {case.name} seed {case.seed}", flush=True)
+    data = W.make_prefill(case)
+    d = _dev(data)
+    out, final = _call(d)
+    torch.cuda.synchronize()
+    _compare(data, out, final)
+
+
+@pytest.mark.parametrize("lens,H,init", [
+    ([1, 63, 64, 65, 200, 0, 130], 3, "per_seq"),
+    ([64], 1, None),
+    ([5], 2, "per_seq"),
+    ([127, 1, 129], 2, None),
+])
+def test_prefill_ragged_varlen(lens, H, init):
+    case = W.PrefillCase(f"ragged_{len(lens)}_h{H}", lens, H, init=init, seed=3000 + sum(lens) + H)
+    print(f"case {case.name} lens {lens}", flush=True)
+    data = W.make_prefill(case)
+    d = _dev(data)
+    out, final = _call(d)
+    torch.cuda.synchronize()
+    _compare(data, out, final)
+
+
+def test_prefill_pool_gather_and_bad_index():
+    case = W.PrefillCase("pool_gather", [70, 100, 33], 2, init="pool", pool_slots=6, seed=3101)
+    data = W.make_prefill(case)
+    data["initial_state_idx"] = torch.tensor([4, -1, 6], dtype=torch.int32)   # -1 and 6 start from zero
+    d = _dev(data)
+    out, final = _call(d)
+    torch.cuda.synchronize()
+    _compare(data, out, final)
+
+
+@pytest.mark.parametrize("lb", [0.0, -1.0, -5.0])
+def test_prefill_lower_bound_values(lb):
+    case = W.PrefillCase(f"lb_{lb}", [150, 90], 2, init="per_seq", seed=3102, lower_bound=lb)
+    data = W.make_prefill(case)
+    d = _dev(data)
+    out, final = _call(d)
+    torch.cuda.synchronize()
+    _compare(data, out, final)
+
+
+def test_prefill_writes_only_its_rows_and_handles_empty():
+    case = W.PrefillCase("canary", [0, 77, 0], 2, init="per_seq", seed=3103)
+    data = W.make_prefill(case)
+    d = _dev(data)
+    T = 77
+    big = torch.full((T + 8, 2, 128), 5.0, dtype=torch.bfloat16, device="cuda")
+    out_view = big[4:4 + T]
+    fin = torch.full((3, 2, 128, 128), 9.0, dtype=torch.float32, device="cuda")
+    _call(d, out=out_view, final_state=fin)
+    torch.cuda.synchronize()
+    assert torch.all(big[:4] == 5.0) and torch.all(big[4 + T:] == 5.0)
+    _compare(data, out_view, fin)
+    # empty sequences copy their start state
+    assert torch.equal(fin[0], d["initial_state"][0]) and torch.equal(fin[2], d["initial_state"][2])
+
+
+def test_prefill_no_tokens_only_state_copy():
+    case = W.PrefillCase("empty_all", [0, 0], 2, init="per_seq", seed=3104)
+    data = W.make_prefill(case)
+    d = _dev(data)
+    out, fin = _call(d)
+    torch.cuda.synchronize()
+    assert out.shape[0] == 0
+    assert torch.equal(fin, d["initial_state"])
+
+
+def test_prefill_strided_inputs_bitwise_equal_dense():
+    case = W.PrefillCase("strided", [100, 160], 4, init="per_seq", seed=3105)
+    data = W.make_prefill(case)
+    d = _dev(data)
+    T, H = 260, 4
+    fused = torch.empty((T, 4 * H * 128 + 64), dtype=torch.bfloat16, device="cuda")
+    views = {}
+    for i, name in enumerate(("q", "k", "v", "g")):
+        fused[:, i * H * 128:(i + 1) * H * 128] = d[name].reshape(T, H * 128)
+        views[name] = fused[:, i * H * 128:(i + 1) * H * 128].view(T, H, 128)
+    o1, f1 = _call(d)
+    o2, f2 = _call(dict(d, **views))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+
+
+def test_prefill_deterministic():
+    data = W.make_prefill(W.PrefillCase("det", [300, 200, 500], 8, init="per_seq", seed=3106))
+    d = _dev(data)
+    o1, f1 = _call(d)
+    o2, f2 = _call(d)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+
+
+def test_prefill_resume_matches_single_call():
+    """prefill(x[:a]) then prefill(x[a:], start = final) matches prefill(x) (chunk edges differ)."""
+    data = W.make_prefill(W.PrefillCase("resume", [333], 2, init="per_seq", seed=3107))
+    d = _dev(data)
+    o_full, f_full = _call(d)
+    a = 150
+    cuA = torch.tensor([0, a], dtype=torch.int32, device="cuda")
+    cuB = torch.tensor([0, 333 - a], dtype=torch.int32, device="cuda")
+    sl = lambda x, s: x[s]
+    dA = dict(d, q=d["q"][:a], k=d["k"][:a], v=d["v"][:a], g=d["g"][:a],
+              beta_logits=d["beta_logits"][:a], cu_seqlens=cuA)
+    oA, fA = _call(dA)
+    dB = dict(d, q=d["q"][a:], k=d["k"][a:], v=d["v"][a:], g=d["g"][a:],
+              beta_logits=d["beta_logits"][a:], cu_seqlens=cuB, initial_state=fA)
+    oB, fB = _call(dB)
+    torch.cuda.synchronize()
+    o_ref, f_ref, _ = _oracle(data)
+    TOL.assert_output_ok(torch.cat([oA, oB]), o_ref)
+    TOL.assert_state_ok(fB, f_ref)
+    TOL.assert_output_ok(o_full, o_ref)
+
+
+def test_prefill_final_state_in_place_over_initial():
+    data = W.make_prefill(W.PrefillCase("inplace", [90, 190], 2, init="per_seq", seed=3108))
+    d = _dev(data)
+    o_ref_gpu, f_ref_gpu = _call(d)
+    pool = d["initial_state"].clone()
+    o2, f2 = _call(dict(d, initial_state=pool), final_state=pool)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o_ref_gpu) and torch.equal(pool, f_ref_gpu)
+
+
+def test_prefill_matches_verify_on_block_sequences():
+    """Verify rows of T tokens and prefill of sequences of T tokens from the same pool states
+    both match the oracle (each output is rounded to bf16 once, so they are compared
+    to the fp64 reference rather than to each other)."""
+    vcase = W.VerifyCase("pv", 6, 8, 4, pool_slots=10, seed=3109)
+    vdata = W.make_verify(vcase)
+    vd = _dev(vdata)
+    ov, iv = recurrent_verify(vd["q"], vd["k"], vd["v"], vd["g"], vd["beta_logits"], vd["A_log"],
+                              vd["dt_bias"], vd["lower_bound"], vd["state_pool"], vd["state_idx"], 8)
+    cu = torch.arange(0, 49, 8, dtype=torch.int32, device="cuda")
+    op, fp = chunk_prefill(vd["q"], vd["k"], vd["v"], vd["g"], vd["beta_logits"], vd["A_log"],
+                           vd["dt_bias"], vd["lower_bound"], cu, initial_state=vd["state_pool"],
+                           initial_state_idx=vd["state_idx"])
+    torch.cuda.synchronize()
+    f = W.to_f64
+    o_ref, i_ref = O.recurrent_verify(f(vdata["q"]), f(vdata["k"]), f(vdata["v"]), f(vdata["g"]),
+                                      f(vdata["beta_logits"]), f(vdata["A_log"]),
+                                      f(vdata["dt_bias"]), vdata["lower_bound"],
+                                      vdata["state_pool"].numpy(), vdata["state_idx"].numpy(), 8)
+    TOL.assert_output_ok(op, o_ref)
+    TOL.assert_output_ok(ov, o_ref)
+    TOL.assert_state_ok(fp, i_ref[:, -1])
+    TOL.assert_state_ok(iv[:, -1], i_ref[:, -1])
+
+
+# ---------------------------------------------------------------- full workload sizes (sampled heads)
+
+FULL = [
+    (W.VARLEN, [0, 9], [0, 7]),
+    (W.LONG, [3, 12], [0, 3]),
+    (W.SINGLE_LONG, [5], [0]),
+]
+
+
+@pytest.mark.parametrize("case,heads,seqs", FULL, ids=[c[0].name for c in FULL])
+def test_prefill_full_size_sampled(case, heads, seqs):
+    print(f"case {case.name} seed {case.seed} heads {heads} seqs {seqs}", flush=True)
+    data = W.make_prefill(case)
+    d = _dev(data)
+    out = None
+    if case.init == "pool":
+        # the layer buffer is preallocated and written in place
+        out = torch.empty((d["q"].shape[0], d["q"].shape[1], 128), dtype=torch.bfloat16, device="cuda")
+    o, fin = _call(d, out=out) if out is not None else _call(d)
+    torch.cuda.synchronize()
+    if out is not None:
+        assert o.data_ptr() == out.data_ptr()
+    _compare(data, o, fin, heads=heads, seqs=seqs)
