@@ -30,8 +30,10 @@ What it computes (the plain definition, token by token, in float64):
 Readings taken where the pages are silent:
 L2 norm is x / sqrt(sum(x^2) + 1e-6); scale defaults to 1/sqrt(d_k); state
 layout is [K, V] (rows are key channels, the ones the gate decays); a
-zero-length sequence leaves its state untouched; a negative state index marks
-a padding row whose outputs are zero and whose states are not written.
+zero-length sequence leaves its state untouched; in verify, a state index
+outside [0, slots) marks a padding row whose outputs are zero and whose
+states are not written; in prefill, a start-state index outside the pool
+starts that sequence from the zero state.
 
 Parity pins for every function here live in ``tests/test_oracle_pins.py``.
 """
@@ -143,7 +145,8 @@ def chunk_prefill(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, cu_seqle
             init = _as64(initial_state)
             for j, n in enumerate(seqs):
                 row = n if initial_state_idx is None else int(initial_state_idx[n])
-                S[j] = init[row]
+                if 0 <= row < init.shape[0]:
+                    S[j] = init[row]
         S = S.reshape(len(seqs) * H, K, V)
         starts = np.array([cu[n] for n in seqs])
         for t in range(length):
@@ -160,7 +163,7 @@ def recurrent_verify(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound,
                      state_pool, state_idx, num_steps, scale=None):
     """Multi-step verify: B rows of num_steps tokens each (token b*T + t).
 
-    state_pool: [slots, H, K, V] (read only); state_idx: [B] ints, negative = padding.
+    state_pool: [slots, H, K, V] (read only); state_idx: [B] ints, outside [0, slots) = padding.
     Returns (out [B*T, H, V], intermediate [B, T, H, K, V]) where
     intermediate[b, t] is the state after token t of row b.  Padding rows give
     zero outputs and zero intermediate rows (the GPU leaves them unwritten).
@@ -175,10 +178,10 @@ def recurrent_verify(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound,
     idx = np.asarray(state_idx).reshape(-1)
     out = np.zeros((BT, H, V), dtype=np.float64)
     inter = np.zeros((B, T, H, K, V), dtype=np.float64)
-    live = [b for b in range(B) if int(idx[b]) >= 0]
+    pool = np.asarray(state_pool)
+    live = [b for b in range(B) if 0 <= int(idx[b]) < pool.shape[0]]
     if not live:
         return out, inter
-    pool = np.asarray(state_pool)
     S = np.stack([pool[int(idx[b])].astype(np.float64) for b in live]).reshape(-1, K, V)
 
     qn = l2_normalize(q)

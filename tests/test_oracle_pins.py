@@ -327,6 +327,21 @@ def test_state_index_gather():
     assert np.array_equal(o, o2) and np.array_equal(f, f2)
 
 
+def test_out_of_range_indices():
+    """Verify: an index outside [0, slots) is a padding row (zero output, zero rows).
+    Prefill: a start index outside the pool starts from the zero state."""
+    B, T, H, K, V = 3, 4, 1, 8, 8
+    q, k, v, g, bl, A_log, dt, lb = _rand_inputs(B * T, H, K, V, np.random.default_rng(12))
+    pool = RNG.standard_normal((2, H, K, V))
+    o, inter = O.recurrent_verify(q, k, v, g, bl, A_log, dt, lb, pool, np.array([1, 2, -3]), T)
+    assert np.all(o[T:] == 0) and np.all(inter[1:] == 0) and np.any(o[:T] != 0)
+    cu = np.array([0, 5, 12])
+    o1, f1 = O.chunk_prefill(q[:12], k[:12], v[:12], g[:12], bl[:12], A_log, dt, lb, cu, pool,
+                             initial_state_idx=np.array([7, -1]))
+    o2, f2 = O.chunk_prefill(q[:12], k[:12], v[:12], g[:12], bl[:12], A_log, dt, lb, cu, None)
+    assert np.array_equal(o1, o2) and np.array_equal(f1, f2)
+
+
 def test_verify_equals_prefill_and_rows():
     B, T, H, K, V = 3, 5, 2, 16, 16
     q, k, v, g, bl, A_log, dt, lb = _rand_inputs(B * T, H, K, V, np.random.default_rng(11))
