@@ -1,0 +1,258 @@
+"""KDA prefill + verify benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step is one pass of the whole hot path over one batch of synthetic input:
+  * varlen chunked prefill of 4 sequences x 8192 tokens, H = 16, d = 128
+    (zero start state, fp32 final states): the intra-chunk kernel then the
+    state-scan kernel (kda_chunk_prefill_intra + kda_chunk_prefill_scan, which
+    together are exactly kda_chunk_prefill);
+  * fused verify of 64 rows x 8 draft tokens, H = 16, states gathered from a
+    256-slot fp32 pool, per-step fp32 states written (kda_recurrent_verify).
+Inputs are resident in HBM before timing starts.  Each kernel is bracketed by
+HIP events on the stream it is launched on (torch's current stream, which the
+binding hands to libkda).  Prints ONE JSON line on stdout; progress goes to stderr.
+
+`value` is prefill tokens/s at 4x8192 (the headline shape); prefill and verify
+microseconds per layer are reported beside it.  The oracle (fp64 CPU token
+loop) is timed on a bounded sample of the same prefill workload as
+`cpu_baseline`.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import resource
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from linear_attention_rule_amd import chunk_prefill, prefill_workspace_bytes, recurrent_verify  # noqa: E402
+from linear_attention_rule_amd import workloads as W  # noqa: E402
+
+METRIC = "KDA prefill µs/layer & tokens/s (8192x4, H=16, d=128); verify µs/layer"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16/fp16 MFMA
+D = 128
+# Algorithmic bytes per token-head: q, k, v, g (bf16, 4 x 256 B) + beta logit (2 B) + out (256 B).
+BYTES_PER_TOKEN_HEAD = 4 * 2 * D + 2 + 2 * D
+STATE_BYTES = 4 * D * D
+# Algorithmic prefill MFMA flops per token-head at chunk 64 (triangular products at half).
+FLOPS_PER_TOKEN_HEAD = 5 * 64 * D + 6 * D * D
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_dev(data):
+    return {k: (v.to("cuda") if isinstance(v, torch.Tensor) else v) for k, v in data.items()}
+
+
+def cpu_baseline(case, tokens_per_seq):
+    """Time the fp64 oracle on all sequences x all heads of `case`, first `tokens_per_seq` tokens."""
+    from oracle import kda_oracle as O
+    data = W.make_prefill(case)
+    cu = data["cu_seqlens"].numpy().astype(np.int64)
+    rows = np.concatenate([np.arange(cu[n], cu[n] + tokens_per_seq) for n in range(len(cu) - 1)])
+    f = W.to_f64
+    sub_cu = np.arange(0, len(rows) + 1, tokens_per_seq)
+    args = (f(data["q"])[rows], f(data["k"])[rows], f(data["v"])[rows], f(data["g"])[rows],
+            f(data["beta_logits"])[rows], f(data["A_log"]), f(data["dt_bias"]), data["lower_bound"],
+            sub_cu)
+    r0 = resource.getrusage(resource.RUSAGE_SELF)
+    t0 = time.perf_counter()
+    O.chunk_prefill(*args, scale=data["scale"])
+    wall = time.perf_counter() - t0
+    r1 = resource.getrusage(resource.RUSAGE_SELF)
+    cpu = (r1.ru_utime - r0.ru_utime) + (r1.ru_stime - r0.ru_stime)
+    tokens = len(rows)
+    return {"value": tokens / wall, "unit": "tokens/s", "cores": max(1, round(cpu / wall)),
+            "kind": "oracle",
+            "sample": f"{case.name}: all {len(cu) - 1} sequences x {case.heads} heads, first "
+                      f"{tokens_per_seq} tokens of each ({tokens} tokens, {wall:.1f} s wall, "
+                      f"fp64 numpy token loop, {os.cpu_count()} host CPUs visible)"}
+
+
+def roofline(bytes_, flops, seconds, bound="hbm"):
+    if bound == "hbm":
+        ach = bytes_ / seconds / 1e9
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+    ach = flops / seconds / 1e12
+    return {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+            "frac": round(ach / MFMA_BF16_PEAK_TFS, 4), "traffic": None}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=2048,
+                    help="tokens per sequence in the oracle's timed sample")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    pcase, vcase = W.LONG, W.VERIFY
+    log(f"generating {pcase.name} and {vcase.name}")
+    pd = to_dev(W.make_prefill(pcase))
+    vd = to_dev(W.make_verify(vcase))
+    T, H = pd["q"].shape[0], pd["q"].shape[1]
+    N = pd["cu_seqlens"].numel() - 1
+    ws = torch.empty(prefill_workspace_bytes(N, T, H), dtype=torch.uint8, device="cuda")
+    out = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
+    fin = torch.empty((N, H, D, D), dtype=torch.float32, device="cuda")
+    B, Tv = vcase.batch, vcase.steps
+    vout = torch.empty((B * Tv, H, D), dtype=torch.bfloat16, device="cuda")
+    inter = torch.empty((B, Tv, H, D, D), dtype=torch.float32, device="cuda")
+
+    def prefill(phase):
+        chunk_prefill(pd["q"], pd["k"], pd["v"], pd["g"], pd["beta_logits"], pd["A_log"],
+                      pd["dt_bias"], pd["lower_bound"], pd["cu_seqlens"], out=out, final_state=fin,
+                      workspace=ws, scale=pd["scale"], phase=phase)
+
+    def verify():
+        recurrent_verify(vd["q"], vd["k"], vd["v"], vd["g"], vd["beta_logits"], vd["A_log"],
+                         vd["dt_bias"], vd["lower_bound"], vd["state_pool"], vd["state_idx"], Tv,
+                         intermediate=inter, out=vout, scale=vd["scale"])
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        prefill("intra")
+        if ev is not None:
+            ev[1].record()
+        prefill("scan")
+        if ev is not None:
+            ev[2].record()
+        verify()
+        if ev is not None:
+            ev[3].record()
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    t_intra = [e[0].elapsed_time(e[1]) * 1e-3 for e in evs]
+    t_scan = [e[1].elapsed_time(e[2]) * 1e-3 for e in evs]
+    t_ver = [e[2].elapsed_time(e[3]) * 1e-3 for e in evs]
+    s_intra, s_scan, s_ver = (float(np.mean(x)) for x in (t_intra, t_scan, t_ver))
+    s_prefill = s_intra + s_scan
+    log(f"intra {s_intra * 1e6:.1f} us  scan {s_scan * 1e6:.1f} us  verify {s_ver * 1e6:.1f} us")
+
+    # Cold-cache pass: overwrite 1 GiB between iterations (outside the events).
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    cold_p, cold_v = [], []
+    for _ in range(5):
+        flush.fill_(1.0)
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        e0.record()
+        prefill("both")
+        e1.record()
+        flush.fill_(2.0)
+        torch.cuda.synchronize()
+        e1b = torch.cuda.Event(enable_timing=True)
+        e1b.record()
+        verify()
+        e2.record()
+        torch.cuda.synchronize()
+        cold_p.append(e0.elapsed_time(e1) * 1e-3)
+        cold_v.append(e1b.elapsed_time(e2) * 1e-3)
+    del flush
+
+    token_heads = T * H
+    prefill_bytes = token_heads * BYTES_PER_TOKEN_HEAD + N * H * STATE_BYTES   # + final states
+    intra_bytes = token_heads * (3 * 2 * D + 2)                                 # q, k, g, beta logit
+    scan_bytes = token_heads * (2 * D + 2 * D) + N * H * STATE_BYTES            # v, out, final states
+    verify_bytes = (B * Tv * H * BYTES_PER_TOKEN_HEAD + B * H * STATE_BYTES
+                    + B * Tv * H * STATE_BYTES)
+    prefill_flops = token_heads * FLOPS_PER_TOKEN_HEAD
+    kernels = {
+        "kda_prefill_intra": (s_intra, roofline(intra_bytes, 0, s_intra)),
+        "kda_prefill_scan": (s_scan, roofline(scan_bytes, 0, s_scan)),
+        "kda_verify": (s_ver, roofline(verify_bytes, 0, s_ver)),
+    }
+    dom = max(kernels, key=lambda k: kernels[k][0])
+    rl = dict(kernels[dom][1])
+    rl["kernel"] = dom
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"oracle baseline on {args.cpu_tokens} tokens/sequence")
+        cpu = cpu_baseline(pcase, args.cpu_tokens)
+
+    value = T / s_prefill
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"prefill {pcase.name} + verify {vcase.name}",
+            "prefill": {"seqs": N, "seq_len": T // N, "heads": H, "head_dim": D, "chunk": 64,
+                        "initial_state": "zero"},
+            "verify": {"batch": B, "draft_steps": Tv, "heads": H, "pool_slots": vcase.pool_slots},
+            "parallelism": "single GPU",
+            "compute": "bf16 in/out; fp16 and bf16 MFMA operands with fp32 accumulation; fp32 state",
+        },
+        "prefill_us_per_layer": round(s_prefill * 1e6, 2),
+        "prefill_tokens_per_s": round(value, 1),
+        "verify_us_per_layer": round(s_ver * 1e6, 2),
+        "verify_tokens_per_s": round(B * Tv / s_ver, 1),
+        "kernel_us": {"kda_prefill_intra": round(s_intra * 1e6, 2),
+                      "kda_prefill_scan": round(s_scan * 1e6, 2),
+                      "kda_verify": round(s_ver * 1e6, 2)},
+        "cold_cache_us": {"prefill": round(float(np.median(cold_p)) * 1e6, 2),
+                          "verify": round(float(np.median(cold_v)) * 1e6, 2)},
+        "roofline": rl,
+        "roofline_by_kernel": {k: v[1] for k, v in kernels.items()},
+        "roofline_prefill_call": {
+            "hbm": roofline(prefill_bytes, 0, s_prefill),
+            "mfma": roofline(0, prefill_flops, s_prefill, bound="mfma"),
+            "roofline_frac": round(max(prefill_bytes / (HBM_PEAK_GBS * 1e9),
+                                       prefill_flops / (MFMA_BF16_PEAK_TFS * 1e12)) / s_prefill, 4),
+        },
+        "cpu_baseline": cpu,
+        "context": {"flashkda_gb300_us_per_layer_8192x4": 146,
+                    "note": "the pages' number, other hardware; not a target"},
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -117,6 +117,31 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const 
                              const kda_prefill_desc* desc, void* stream);
 
 /*
+ * The two phases of kda_chunk_prefill as separate calls, with the same
+ * arguments and checks.  kda_chunk_prefill(...) is exactly
+ * kda_chunk_prefill_intra(...) followed by kda_chunk_prefill_scan(...) on the
+ * same stream with the same workspace: the intra phase (parallel over chunks
+ * and heads) writes one record per (chunk, head) into the workspace, and the
+ * scan phase (sequential over each sequence's chunks) reads them and writes
+ * out and final_state.  Splitting lets a caller time or schedule the phases
+ * on their own; the workspace contents between them are private to libkda.
+ */
+kda_status kda_chunk_prefill_intra(const void* q, const void* k, const void* v, const void* g,
+                                   const void* beta_logits, const float* A_log,
+                                   const float* dt_bias, float lower_bound,
+                                   const int32_t* cu_seqlens, const float* initial_state,
+                                   const int32_t* initial_state_idx, void* out,
+                                   float* final_state, void* workspace, size_t workspace_bytes,
+                                   const kda_prefill_desc* desc, void* stream);
+kda_status kda_chunk_prefill_scan(const void* q, const void* k, const void* v, const void* g,
+                                  const void* beta_logits, const float* A_log,
+                                  const float* dt_bias, float lower_bound,
+                                  const int32_t* cu_seqlens, const float* initial_state,
+                                  const int32_t* initial_state_idx, void* out,
+                                  float* final_state, void* workspace, size_t workspace_bytes,
+                                  const kda_prefill_desc* desc, void* stream);
+
+/*
  * Fused multi-step verify (TensorRT-LLM PR #21179, fused-verify commit: the
  * fused_recurrent_kda role).  For each row b the state starts from
  * state_pool[state_idx[b]] (the pool is only read) and the T tokens of the row

@@ -70,9 +70,11 @@ def load_library(path: str | None = None):
     lib.kda_last_error.argtypes = []
     lib.kda_chunk_prefill_workspace_size.restype = sz
     lib.kda_chunk_prefill_workspace_size.argtypes = [i32, i32, i32, i32]
-    lib.kda_chunk_prefill.restype = ctypes.c_int
-    lib.kda_chunk_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, vp, sz,
-                                      ctypes.POINTER(PrefillDesc), vp]
+    for name in ("kda_chunk_prefill", "kda_chunk_prefill_intra", "kda_chunk_prefill_scan"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, vp, sz,
+                       ctypes.POINTER(PrefillDesc), vp]
     lib.kda_recurrent_verify.restype = ctypes.c_int
     lib.kda_recurrent_verify.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp,
                                          ctypes.POINTER(VerifyDesc), vp]
@@ -148,8 +150,13 @@ def prefill_workspace_bytes(num_seqs: int, total_tokens: int, num_heads: int) ->
 
 def chunk_prefill(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, cu_seqlens, *,
                   initial_state=None, initial_state_idx=None, out=None, final_state=None,
-                  write_final_state=True, scale=None, workspace=None, check=False):
+                  write_final_state=True, scale=None, workspace=None, check=False,
+                  phase="both"):
     """Varlen chunked KDA prefill.  Returns (out, final_state or None).
+
+    phase: "both" (kda_chunk_prefill), or "intra" / "scan" for the two halves of
+    the same call (kda_chunk_prefill_intra / kda_chunk_prefill_scan), which must
+    then be given the same workspace.
 
     q, k, v, g: bf16 [T, H, 128] (token stride free, heads dense); beta_logits bf16 [T, H];
     A_log f32 [H]; dt_bias f32 [H, 128]; cu_seqlens int32 [N+1] on the device.
@@ -198,7 +205,9 @@ def chunk_prefill(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, cu_seqle
             raise ValueError("cu_seqlens must start at 0, be non-decreasing and end at T")
     desc = PrefillDesc(N, T, H, HEAD_DIM, float(scale) if scale else 0.0, rows,
                        qs, ks, vs, gs, bs, os_)
-    st = lib.kda_chunk_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta_logits), _ptr(A_log),
+    fn = {"both": lib.kda_chunk_prefill, "intra": lib.kda_chunk_prefill_intra,
+          "scan": lib.kda_chunk_prefill_scan}[phase]
+    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta_logits), _ptr(A_log),
                                _ptr(dt_bias), float(lower_bound), _ptr(cu_seqlens),
                                _ptr(initial_state), _ptr(initial_state_idx), _ptr(out),
                                _ptr(final_state), _ptr(workspace),

@@ -80,12 +80,17 @@ size_t kda_chunk_prefill_workspace_size(int32_t num_seqs, int32_t total_tokens, 
          static_cast<size_t>(num_heads) * static_cast<size_t>(kda::REC_BYTES);
 }
 
-kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const void* g,
-                             const void* beta_logits, const float* A_log, const float* dt_bias,
-                             float lower_bound, const int32_t* cu_seqlens,
-                             const float* initial_state, const int32_t* initial_state_idx,
-                             void* out, float* final_state, void* workspace,
-                             size_t workspace_bytes, const kda_prefill_desc* desc, void* stream) {
+}  // extern "C"
+
+namespace {
+
+kda_status prefill_phases(const void* q, const void* k, const void* v, const void* g,
+                          const void* beta_logits, const float* A_log, const float* dt_bias,
+                          float lower_bound, const int32_t* cu_seqlens,
+                          const float* initial_state, const int32_t* initial_state_idx,
+                          void* out, float* final_state, void* workspace,
+                          size_t workspace_bytes, const kda_prefill_desc* desc, void* stream,
+                          int phases) {
   if (!desc) return fail(KDA_ERR_INVALID_ARGUMENT, "desc is NULL");
   const int N = desc->num_seqs, T = desc->total_tokens, H = desc->num_heads;
   if (desc->head_dim != KDA_HEAD_DIM)
@@ -155,9 +160,33 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const 
   p.num_slots_chunk = static_cast<int>(kda::chunk_slots(N, T));
   p.init_rows = desc->num_state_rows;
   p.q_st = qs; p.k_st = ks; p.v_st = vs; p.g_st = gs; p.b_st = bs; p.o_st = os;
-  const hipError_t e = kda::launch_prefill(p, static_cast<hipStream_t>(stream));
+  const hipError_t e = kda::launch_prefill(p, phases, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+#define KDA_PREFILL_ARGS                                                                      \
+  const void *q, const void *k, const void *v, const void *g, const void *beta_logits,       \
+      const float *A_log, const float *dt_bias, float lower_bound, const int32_t *cu_seqlens, \
+      const float *initial_state, const int32_t *initial_state_idx, void *out,               \
+      float *final_state, void *workspace, size_t workspace_bytes,                           \
+      const kda_prefill_desc *desc, void *stream
+#define KDA_PREFILL_FWD                                                                     \
+  q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, cu_seqlens, initial_state,          \
+      initial_state_idx, out, final_state, workspace, workspace_bytes, desc, stream
+
+kda_status kda_chunk_prefill(KDA_PREFILL_ARGS) {
+  return prefill_phases(KDA_PREFILL_FWD, kda::PHASE_INTRA | kda::PHASE_SCAN);
+}
+kda_status kda_chunk_prefill_intra(KDA_PREFILL_ARGS) {
+  return prefill_phases(KDA_PREFILL_FWD, kda::PHASE_INTRA);
+}
+kda_status kda_chunk_prefill_scan(KDA_PREFILL_ARGS) {
+  return prefill_phases(KDA_PREFILL_FWD, kda::PHASE_SCAN);
 }
 
 kda_status kda_recurrent_verify(const void* q, const void* k, const void* v, const void* g,

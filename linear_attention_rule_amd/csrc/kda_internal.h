@@ -91,6 +91,9 @@ inline int64_t chunk_slots(int N, int T_total) { return static_cast<int64_t>(T_t
 
 // Launchers (enqueue only; return the hipGetLastError() of the launch).
 hipError_t launch_verify(const VerifyParams& p, hipStream_t s);
-hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
+// Prefill phases: bit 0 = intra-chunk kernel, bit 1 = state-scan kernel.
+constexpr int PHASE_INTRA = 1;
+constexpr int PHASE_SCAN = 2;
+hipError_t launch_prefill(const PrefillParams& p, int phases, hipStream_t s);
 
 }  // namespace kda

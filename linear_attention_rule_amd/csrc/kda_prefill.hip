@@ -143,43 +143,44 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
   const int L = min(CHUNK, ce - t0);
   unsigned char* rec = p.work + (static_cast<int64_t>(slot) * H + h) * REC_BYTES;
 
-  // ---- a1: loads, norms, gate, beta.
+  // ---- a1: loads, norms, gate, beta.  Rows past the chunk end are read from the
+  // last valid row (always in bounds) and zeroed arithmetically, so no per-lane
+  // branches split the loads.
   const int t = 16 * w + m;
   const bool valid = t < L;
-  const int64_t tok = static_cast<int64_t>(t0) + t;
+  const float vmask = valid ? 1.f : 0.f;
+  const int64_t tok = static_cast<int64_t>(t0) + min(t, L - 1);
   float qv[32], kv[32], la[32];
   {
-    float gv[32];
-    if (valid) {
-      const uint16_t* qp = p.q + tok * p.q_st + h * D;
-      const uint16_t* kp = p.k + tok * p.k_st + h * D;
-      const uint16_t* gp = p.g + tok * p.g_st + h * D;
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int c0 = kperm(s, g, 4 * hh);
-          load4_bf16(qp + c0, qv + 8 * s + 4 * hh);
-          load4_bf16(kp + c0, kv + 8 * s + 4 * hh);
-          load4_bf16(gp + c0, gv + 8 * s + 4 * hh);
-        }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) qv[i] = kv[i] = gv[i] = 0.f;
-    }
-    const float eA = __builtin_amdgcn_exp2f(p.A_log[h] * LOG2E);
+    float gv[32], dt[32];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        const float4 dt = *reinterpret_cast<const float4*>(p.dt_bias + h * D + kperm(s, g, 4 * hh));
-        const float d4[4] = {dt.x, dt.y, dt.z, dt.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 8 * s + 4 * hh + e;
-          la[i] = valid ? p.lb_log2e * sigmoid_f32(eA * (gv[i] + d4[e])) : 0.f;
-        }
+        const float4 d4 = *reinterpret_cast<const float4*>(p.dt_bias + h * D + kperm(s, g, 4 * hh));
+        float* dd = dt + 8 * s + 4 * hh;
+        dd[0] = d4.x; dd[1] = d4.y; dd[2] = d4.z; dd[3] = d4.w;
       }
+    const uint16_t* qp = p.q + tok * p.q_st + h * D;
+    const uint16_t* kp = p.k + tok * p.k_st + h * D;
+    const uint16_t* gp = p.g + tok * p.g_st + h * D;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int c0 = kperm(s, g, 4 * hh);
+        load4_bf16(qp + c0, qv + 8 * s + 4 * hh);
+        load4_bf16(kp + c0, kv + 8 * s + 4 * hh);
+        load4_bf16(gp + c0, gv + 8 * s + 4 * hh);
+      }
+    const float eA = __builtin_amdgcn_exp2f(p.A_log[h] * LOG2E);
+    const float lbm = p.lb_log2e * vmask;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      qv[i] *= vmask;
+      kv[i] *= vmask;
+      la[i] = lbm * sigmoid_f32(eA * (gv[i] + dt[i]));
+    }
   }
   float ssq = 0.f, ssk = 0.f;
 #pragma unroll
@@ -193,8 +194,7 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
   ssk += __shfl_xor(ssk, 32);
   const float rq = __builtin_amdgcn_rsqf(ssq + L2_EPS);
   const float rk = __builtin_amdgcn_rsqf(ssk + L2_EPS);
-  if (g == 0)
-    sm.beta[t] = valid ? sigmoid_f32(bf16_to_f32(p.beta[tok * p.b_st + h])) : 0.f;
+  if (g == 0) sm.beta[t] = vmask * sigmoid_f32(bf16_to_f32(p.beta[tok * p.b_st + h]));
 
   // In-block inclusive cumulative log2 decay (lanes m = 0..15 of a row are 16 tokens).
 #pragma unroll
@@ -303,11 +303,15 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
     }
     // lane (n, g) holds rows t = 16w + 4g + r, column i = 16wb + n
     const int i = 16 * wb + m;
+    const float4 b4 = *reinterpret_cast<const float4*>(sm.beta + 16 * w + 4 * g);
+    const float bt[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int tr = 16 * w + 4 * g + r;
-      sm.AT[tr * ATS + i] = (i < tr) ? sm.beta[tr] * accG[r] : 0.f;
-      sm.P[tr * ATS + i] = (i <= tr) ? p.scale * accP[r] : 0.f;
+      const float gval = bt[r] * accG[r];
+      const float pval = p.scale * accP[r];
+      sm.AT[tr * ATS + i] = (i < tr) ? gval : 0.f;
+      sm.P[tr * ATS + i] = (i <= tr) ? pval : 0.f;
     }
   }
   for (int wb = w + 1; wb < 4; ++wb) {
@@ -416,12 +420,33 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
 // Kernel 2: state scan, one workgroup of NW waves per (sequence, head, value slice).
 // ============================================================================
 
+// 16 bytes per lane from global memory straight into LDS (no VGPR staging):
+// lane l's bytes land at lds_dst + 16 l.  Issued as inline asm so the compiler does
+// not track it: the scan loop orders these copies itself with an explicit
+// s_waitcnt vmcnt and a barrier before any wave reads the buffer.
+__device__ __forceinline__ void lds_dma16(const void* gsrc, unsigned char* lds_dst) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned char*)lds_dst)));
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds), "v"(gsrc)
+               : "memory", "m0");
+}
+
+// Async copy of one chunk record into LDS, split over the NW waves of the workgroup.
+// Every wave issues the same compile-time number of 1 KiB copies (the few surplus ones
+// repeat the last fragment, writing identical bytes), so the compiler can count the
+// operations in flight exactly.
+template <int NW>
 __device__ __forceinline__ void copy_record_async(const unsigned char* src, unsigned char* dst,
-                                                  int wave, int nw, int lane) {
-  for (int f = wave; f < REC_BYTES / 1024; f += nw)
-    __builtin_amdgcn_global_load_lds(
-        reinterpret_cast<const void*>(src + f * 1024 + lane * 16),
-        (__attribute__((address_space(3))) void*)(dst + f * 1024), 16, 0, 0);
+                                                  int wave, int lane) {
+  constexpr int NF = REC_BYTES / 1024;
+  constexpr int PER_WAVE = (NF + NW - 1) / NW;
+#pragma unroll
+  for (int k = 0; k < PER_WAVE; ++k) {
+    const int f = min(wave + k * NW, NF - 1);
+    lds_dma16(src + f * 1024 + lane * 16, dst + f * 1024);
+  }
 }
 
 __device__ __forceinline__ half8 frag(const unsigned char* r, int f, int lane) {
@@ -436,19 +461,156 @@ __device__ __forceinline__ half8 pack_f16(f32x4 a, f32x4 b) {
   return h;
 }
 
+// Each LDS buffer holds one chunk record followed by NW per-wave value tiles
+// (64 tokens x 16 value columns, bf16, row-major: 2 KiB per wave).
+constexpr int VT_BYTES = 64 * 16 * 2;
+
+// Async copy of this wave's value tile of one chunk into LDS: lane l copies 16 bytes,
+// row (l >> 1) + 32 i, columns 8 (l & 1) .. +7.  Rows past the chunk end re-read the
+// last valid row (in bounds); the consumer masks them.
+__device__ __forceinline__ void copy_vtile_async(const PrefillParams& p, int tb0, int Lc, int h,
+                                                 int v0, unsigned char* dst, int lane) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = min((lane >> 1) + 32 * i, Lc - 1);
+    const uint16_t* src = p.v + static_cast<int64_t>(tb0 + row) * p.v_st + h * D + v0 + 8 * (lane & 1);
+    lds_dma16(src, dst + i * 1024);
+  }
+}
+
+// One chunk of the state scan, reading the record from LDS buffer R.
+__device__ __forceinline__ void scan_chunk(const PrefillParams& p,
+                                           const unsigned char* __restrict__ R,
+                                           const unsigned char* __restrict__ VT, int tb0, int Lc,
+                                           int h, int v0, int lane, f32x4 (&S)[8]) {
+  const int nl = lane & 15, g = lane >> 4;
+  const uint16_t* vt = reinterpret_cast<const uint16_t*>(VT);
+  half8 Sf[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) Sf[s] = pack_f16(S[2 * s], S[2 * s + 1]);
+
+  // X = V - K_Gamma S   (rows = tokens, lane column = value channel)
+  f32x4 X[4];
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tt = 16 * tb + 4 * g + r;
+      const float vv = bf16_to_f32(vt[tt * 16 + nl]);
+      X[tb][r] = (tt < Lc) ? vv : 0.f;
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) X[tb] = mfma_f16(frag(R, FR_KG + 4 * tb + s, lane), Sf[s], X[tb]);
+  }
+  // U = T' X
+  const half8 Xf0 = pack_f16(X[0], X[1]), Xf1 = pack_f16(X[2], X[3]);
+  f32x4 U[4];
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) U[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  U[0] = mfma_f16(frag(R, FR_TP + 0, lane), Xf0, U[0]);
+  U[1] = mfma_f16(frag(R, FR_TP + 1, lane), Xf0, U[1]);
+  U[2] = mfma_f16(frag(R, FR_TP + 2, lane), Xf0, U[2]);
+  U[2] = mfma_f16(frag(R, FR_TP + 3, lane), Xf1, U[2]);
+  U[3] = mfma_f16(frag(R, FR_TP + 4, lane), Xf0, U[3]);
+  U[3] = mfma_f16(frag(R, FR_TP + 5, lane), Xf1, U[3]);
+  const half8 Uf0 = pack_f16(U[0], U[1]), Uf1 = pack_f16(U[2], U[3]);
+
+  // O^T = S^T (scale Q_Gamma)^T + U^T (scale tril P)^T; lane (token, g) holds 4 value columns.
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) o = mfma_f16(Sf[s], frag(R, FR_QG + 4 * tb + s, lane), o);
+    const int fi = (tb < 2) ? tb : 2 + 2 * (tb - 2);
+    o = mfma_f16(Uf0, frag(R, FR_PM + fi, lane), o);
+    if (tb >= 2) o = mfma_f16(Uf1, frag(R, FR_PM + fi + 1, lane), o);
+    const int tt = 16 * tb + nl;
+    if (tt < Lc) {
+      const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16(o[0])) |
+                          (static_cast<uint32_t>(f32_to_bf16(o[1])) << 16);
+      const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16(o[2])) |
+                          (static_cast<uint32_t>(f32_to_bf16(o[3])) << 16);
+      *reinterpret_cast<uint2*>(p.out + static_cast<int64_t>(tb0 + tt) * p.o_st + h * D + v0 +
+                                4 * g) = make_uint2(w0, w1);
+    }
+  }
+  // S <- Diag(Gamma_C) S + K_C^T U
+  const float* gam = reinterpret_cast<const float*>(R + REC_GAMMA_OFF);
+#pragma unroll
+  for (int cb = 0; cb < 8; ++cb) {
+    const float4 gc = *reinterpret_cast<const float4*>(gam + 16 * cb + 4 * g);
+    S[cb][0] *= gc.x;
+    S[cb][1] *= gc.y;
+    S[cb][2] *= gc.z;
+    S[cb][3] *= gc.w;
+    S[cb] = mfma_f16(frag(R, FR_KC + 2 * cb + 0, lane), Uf0, S[cb]);
+    S[cb] = mfma_f16(frag(R, FR_KC + 2 * cb + 1, lane), Uf1, S[cb]);
+  }
+}
+
+// Output stores one wave issues for a full chunk (one 8-byte store per token block).
+// They are issued after the next chunk's copies, and vmcnt counts in issue order,
+// so waiting down to this many outstanding operations guarantees the copies have
+// landed without waiting for the (independent) output stores.
+constexpr int VM_STORES_PER_CHUNK = 4;
+
+// Async copy of chunk jj's record and of this wave's value tile into buffer buf.
+template <int NW>
+__device__ __forceinline__ void copy_chunk_async(const PrefillParams& p,
+                                                 const unsigned char* recbase, int cs, int ce,
+                                                 int jj, int h, int v0, int w, int lane,
+                                                 unsigned char* buf, int vt_off) {
+  copy_record_async<NW>(recbase + static_cast<int64_t>(jj) * p.H * REC_BYTES, buf, w, lane);
+  const int tbj = cs + jj * CHUNK;
+  copy_vtile_async(p, tbj, min(CHUNK, ce - tbj), h, v0, buf + vt_off, lane);
+}
+
+// Chunk j: wait for its copy in `cur`, start chunk j+1's copy into `nxt`, compute chunk j.
+// `cur` and `nxt` are distinct LDS buffers; marking them __restrict__ tells the
+// compiler the reads of `cur` do not depend on the copy in flight into `nxt`.
+template <int NW>
+__device__ __forceinline__ void scan_step(const PrefillParams& p, const unsigned char* recbase,
+                                          int64_t rec_stride, int cs, int ce, int j, int nch,
+                                          int h, int v0, int w, int lane, int vt_off,
+                                          unsigned char* __restrict__ cur,
+                                          unsigned char* __restrict__ nxt, f32x4 (&S)[8]) {
+  (void)rec_stride;
+  if (j == 0) {
+    // First chunk: copy it now and wait for it (nothing to overlap with yet).
+    copy_chunk_async<NW>(p, recbase, cs, ce, 0, h, v0, w, lane, cur, vt_off);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(VM_STORES_PER_CHUNK) : "memory");
+  }
+  // A bare barrier: __syncthreads() would also drain the output stores.
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  if (j + 1 < nch) copy_chunk_async<NW>(p, recbase, cs, ce, j + 1, h, v0, w, lane, nxt, vt_off);
+  scan_chunk(p, cur, cur + vt_off, cs + j * CHUNK, min(CHUNK, ce - cs - j * CHUNK), h, v0, lane,
+             S);
+}
+
 template <int NW>
 __global__ __launch_bounds__(64 * NW) void prefill_scan_kernel(PrefillParams p) {
-  __shared__ __attribute__((aligned(16))) unsigned char srec[2][REC_BYTES];
+  constexpr int BUF_BYTES = REC_BYTES + NW * VT_BYTES;
+  __shared__ __attribute__((aligned(16))) unsigned char srec0[BUF_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char srec1[BUF_BYTES];
   constexpr int BV = 16 * NW;
   constexpr int NVS = D / BV;
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, nl = lane & 15, g = lane >> 4;
-  int blk = blockIdx.x;
-  const int vs = blk % NVS;
-  blk /= NVS;
-  const int h = blk % p.H;
-  const int n = blk / p.H;
+  // XCD-aware order: workgroup ids are dealt round-robin to the 8 XCDs (id % 8),
+  // so the NVS value slices of one (sequence, head) pair get ids congruent mod 8
+  // and share one L2 for the record they all read.
   const int H = p.H;
+  const int pairs = p.N * H;
+  const int blk = blockIdx.x;
+  const int grp = blk / (8 * NVS), rr = blk % (8 * NVS);
+  const int vs = rr / 8;
+  const int pair = grp * 8 + (rr & 7);
+  if (pair >= pairs) return;
+  const int n = pair / H;
+  const int h = pair % H;
   const int v0 = vs * BV + 16 * w;     // this wave's 16 value columns
   const int cs = p.cu[n], ce = p.cu[n + 1];
   const int len = ce - cs;
@@ -482,78 +644,14 @@ __global__ __launch_bounds__(64 * NW) void prefill_scan_kernel(PrefillParams p) 
 
   const unsigned char* recbase = p.work + (slot0 * H + h) * REC_BYTES;
   const int64_t rec_stride = static_cast<int64_t>(H) * REC_BYTES;
-  if (nch > 0) copy_record_async(recbase, srec[0], w, NW, lane);
-
-  for (int j = 0; j < nch; ++j) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (j + 1 < nch) copy_record_async(recbase + (j + 1) * rec_stride, srec[(j + 1) & 1], w, NW, lane);
-    const unsigned char* R = srec[j & 1];
-    const int tb0 = cs + j * CHUNK;
-    const int Lc = min(CHUNK, ce - tb0);
-
-    half8 Sf[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) Sf[s] = pack_f16(S[2 * s], S[2 * s + 1]);
-
-    // X = V - K_Gamma S   (rows = tokens, lane column = value channel)
-    f32x4 X[4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tt = 16 * tb + 4 * g + r;
-        X[tb][r] = (tt < Lc)
-                       ? bf16_to_f32(p.v[static_cast<int64_t>(tb0 + tt) * p.v_st + h * D + v0 + nl])
-                       : 0.f;
-      }
-#pragma unroll
-      for (int s = 0; s < 4; ++s) X[tb] = mfma_f16(frag(R, FR_KG + 4 * tb + s, lane), Sf[s], X[tb]);
-    }
-    // U = T' X
-    const half8 Xf0 = pack_f16(X[0], X[1]), Xf1 = pack_f16(X[2], X[3]);
-    f32x4 U[4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) U[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    U[0] = mfma_f16(frag(R, FR_TP + 0, lane), Xf0, U[0]);
-    U[1] = mfma_f16(frag(R, FR_TP + 1, lane), Xf0, U[1]);
-    U[2] = mfma_f16(frag(R, FR_TP + 2, lane), Xf0, U[2]);
-    U[2] = mfma_f16(frag(R, FR_TP + 3, lane), Xf1, U[2]);
-    U[3] = mfma_f16(frag(R, FR_TP + 4, lane), Xf0, U[3]);
-    U[3] = mfma_f16(frag(R, FR_TP + 5, lane), Xf1, U[3]);
-    const half8 Uf0 = pack_f16(U[0], U[1]), Uf1 = pack_f16(U[2], U[3]);
-
-    // O^T = S^T (scale Q_Gamma)^T + U^T (scale tril P)^T; lane (token, g) holds 4 value columns.
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) o = mfma_f16(Sf[s], frag(R, FR_QG + 4 * tb + s, lane), o);
-      const int fi = (tb < 2) ? tb : 2 + 2 * (tb - 2);
-      o = mfma_f16(Uf0, frag(R, FR_PM + fi, lane), o);
-      if (tb >= 2) o = mfma_f16(Uf1, frag(R, FR_PM + fi + 1, lane), o);
-      const int tt = 16 * tb + nl;
-      if (tt < Lc) {
-        const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16(o[0])) |
-                            (static_cast<uint32_t>(f32_to_bf16(o[1])) << 16);
-        const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16(o[2])) |
-                            (static_cast<uint32_t>(f32_to_bf16(o[3])) << 16);
-        *reinterpret_cast<uint2*>(p.out + static_cast<int64_t>(tb0 + tt) * p.o_st + h * D + v0 +
-                                  4 * g) = make_uint2(w0, w1);
-      }
-    }
-    // S <- Diag(Gamma_C) S + K_C^T U
-    const float* gam = reinterpret_cast<const float*>(R + REC_GAMMA_OFF);
-#pragma unroll
-    for (int cb = 0; cb < 8; ++cb) {
-      const float4 gc = *reinterpret_cast<const float4*>(gam + 16 * cb + 4 * g);
-      S[cb][0] *= gc.x;
-      S[cb][1] *= gc.y;
-      S[cb][2] *= gc.z;
-      S[cb][3] *= gc.w;
-      S[cb] = mfma_f16(frag(R, FR_KC + 2 * cb + 0, lane), Uf0, S[cb]);
-      S[cb] = mfma_f16(frag(R, FR_KC + 2 * cb + 1, lane), Uf1, S[cb]);
-    }
+  const int vt_off = REC_BYTES + w * VT_BYTES;
+  // Two chunks per trip so each half reads one fixed LDS buffer while the other
+  // half's buffer is being filled.
+  for (int j = 0; j < nch; j += 2) {
+    scan_step<NW>(p, recbase, rec_stride, cs, ce, j, nch, h, v0, w, lane, vt_off, srec0, srec1, S);
+    if (j + 1 >= nch) break;
+    scan_step<NW>(p, recbase, rec_stride, cs, ce, j + 1, nch, h, v0, w, lane, vt_off, srec1, srec0,
+                  S);
   }
 
   if (p.final_state) {
@@ -567,21 +665,24 @@ __global__ __launch_bounds__(64 * NW) void prefill_scan_kernel(PrefillParams p) 
 
 template <int NW>
 hipError_t launch_scan(const PrefillParams& p, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(p.N) * p.H * (D / (16 * NW)));
+  const int64_t pairs = static_cast<int64_t>(p.N) * p.H;
+  const int64_t groups = (pairs + 7) / 8;
+  const dim3 grid(static_cast<unsigned>(groups * 8 * (D / (16 * NW))));
   hipLaunchKernelGGL(prefill_scan_kernel<NW>, grid, dim3(64 * NW), 0, s, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillParams& p, hipStream_t s) {
+hipError_t launch_prefill(const PrefillParams& p, int phases, hipStream_t s) {
   if (p.N == 0) return hipSuccess;
-  if (p.num_slots_chunk > 0 && p.T_total > 0) {
+  if ((phases & PHASE_INTRA) && p.num_slots_chunk > 0 && p.T_total > 0) {
     const dim3 grid(static_cast<unsigned>(p.num_slots_chunk), static_cast<unsigned>(p.H));
     hipLaunchKernelGGL(prefill_intra_kernel, grid, dim3(256), 0, s, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (!(phases & PHASE_SCAN)) return hipSuccess;
   // Value-slice width per workgroup: enough workgroups to cover the 256 compute
   // units (one resident workgroup per CU: the double-buffered records use 122 KiB of LDS).
   const int64_t pairs = static_cast<int64_t>(p.N) * p.H;

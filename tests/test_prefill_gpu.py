@@ -50,12 +50,7 @@ def _oracle(data, heads=None, seqs=None):
             sub_init = init.numpy()[seqs][:, heads]
         else:
             sub_init = init.numpy()[:, heads]
-            sub_idx = idx.numpy()[seqs]
-            # indices outside the pool start from zero
-            bad = (sub_idx < 0) | (sub_idx >= sub_init.shape[0])
-            if bad.any():
-                sub_init = np.concatenate([sub_init, np.zeros((1,) + sub_init.shape[1:])])
-                sub_idx = np.where(bad, sub_init.shape[0] - 1, sub_idx)
+            sub_idx = idx.numpy()[seqs]       # out-of-pool indices start from zero in the oracle
     o, fs = O.chunk_prefill(pick(data["q"]), pick(data["k"]), pick(data["v"]), pick(data["g"]),
                             f(data["beta_logits"])[rows][:, heads], f(data["A_log"])[heads],
                             f(data["dt_bias"])[heads], data["lower_bound"], sub_cu, sub_init,
