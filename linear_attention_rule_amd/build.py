@@ -27,6 +27,9 @@ HIP_FLAGS = [
     "-Wall",
     "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: the kernels post-process every accumulator tile
+    # with VALU code, and the AGPR form would copy each one back and forth.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -52,6 +52,10 @@ kda_status check_stride(const char* name, int64_t stride, int64_t dense, int64_t
   if (stride == 0) stride = dense;
   if (stride < row_elems) return fail(KDA_ERR_INVALID_ARGUMENT, "%s token stride %lld < %lld", name,
                                       static_cast<long long>(stride), static_cast<long long>(row_elems));
+  // Kernels address up to 64 rows of a chunk with 32-bit byte offsets.
+  if (stride > (int64_t{1} << 24))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "%s token stride %lld exceeds 2^24 elements", name,
+                static_cast<long long>(stride));
   *eff = stride;
   return KDA_OK;
 }

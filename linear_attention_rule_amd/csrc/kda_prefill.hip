@@ -421,31 +421,45 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
 // ============================================================================
 
 // 16 bytes per lane from global memory straight into LDS (no VGPR staging):
-// lane l's bytes land at lds_dst + 16 l.  Issued as inline asm so the compiler does
-// not track it: the scan loop orders these copies itself with an explicit
-// s_waitcnt vmcnt and a barrier before any wave reads the buffer.
-__device__ __forceinline__ void lds_dma16(const void* gsrc, unsigned char* lds_dst) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned char*)lds_dst)));
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+// lane l's bytes land at LDS address lds + 16 l.  The global address is a
+// wave-uniform base (SGPR pair) plus a per-lane 32-bit byte offset.  Issued as
+// inline asm so the compiler does not track it: the scan loop orders these copies
+// itself with an explicit s_waitcnt vmcnt and a barrier before any wave reads
+// the buffer.
+__device__ __forceinline__ void lds_dma16(uint64_t gbase, uint32_t lane_off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
-               : "s"(lds), "v"(gsrc)
+               : "s"(lds), "v"(lane_off), "s"(gbase)
                : "memory", "m0");
 }
 
-// Async copy of one chunk record into LDS, split over the NW waves of the workgroup.
-// Every wave issues the same compile-time number of 1 KiB copies (the few surplus ones
-// repeat the last fragment, writing identical bytes), so the compiler can count the
-// operations in flight exactly.
+__device__ __forceinline__ uint64_t uniform_addr(const void* p) {
+  const uint64_t a = reinterpret_cast<uintptr_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// LDS byte address of a __shared__ object (computed once; no per-use cast).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) unsigned char*)p)));
+}
+
+// Async copy of one chunk record into LDS, split over the NW waves of the workgroup:
+// wave w copies the contiguous fragments [w*PER, (w+1)*PER), all waves the same
+// compile-time count (surplus copies repeat the last fragment, writing identical
+// bytes), so the number of operations in flight is known exactly.
 template <int NW>
-__device__ __forceinline__ void copy_record_async(const unsigned char* src, unsigned char* dst,
-                                                  int wave, int lane) {
+__device__ __forceinline__ void copy_record_async(uint64_t src, uint32_t lds, int wave,
+                                                  uint32_t lane_off) {
   constexpr int NF = REC_BYTES / 1024;
-  constexpr int PER_WAVE = (NF + NW - 1) / NW;
+  constexpr int PER = (NF + NW - 1) / NW;
+  const int f0 = wave * PER;
 #pragma unroll
-  for (int k = 0; k < PER_WAVE; ++k) {
-    const int f = min(wave + k * NW, NF - 1);
-    lds_dma16(src + f * 1024 + lane * 16, dst + f * 1024);
+  for (int k = 0; k < PER; ++k) {
+    const uint32_t f = static_cast<uint32_t>(min(f0 + k, NF - 1));
+    lds_dma16(src + f * 1024u, lane_off, lds + f * 1024u);
   }
 }
 
@@ -469,12 +483,13 @@ constexpr int VT_BYTES = 64 * 16 * 2;
 // row (l >> 1) + 32 i, columns 8 (l & 1) .. +7.  Rows past the chunk end re-read the
 // last valid row (in bounds); the consumer masks them.
 __device__ __forceinline__ void copy_vtile_async(const PrefillParams& p, int tb0, int Lc, int h,
-                                                 int v0, unsigned char* dst, int lane) {
+                                                 int v0, uint32_t lds, int lane) {
+  const uint64_t base = uniform_addr(p.v + static_cast<int64_t>(tb0) * p.v_st + h * D + v0);
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int row = min((lane >> 1) + 32 * i, Lc - 1);
-    const uint16_t* src = p.v + static_cast<int64_t>(tb0 + row) * p.v_st + h * D + v0 + 8 * (lane & 1);
-    lds_dma16(src, dst + i * 1024);
+    const uint32_t off = static_cast<uint32_t>((row * p.v_st + 8 * (lane & 1)) * 2);
+    lds_dma16(base, off, lds + i * 1024u);
   }
 }
 
@@ -526,10 +541,8 @@ __device__ __forceinline__ void scan_chunk(const PrefillParams& p,
     if (tb >= 2) o = mfma_f16(Uf1, frag(R, FR_PM + fi + 1, lane), o);
     const int tt = 16 * tb + nl;
     if (tt < Lc) {
-      const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16(o[0])) |
-                          (static_cast<uint32_t>(f32_to_bf16(o[1])) << 16);
-      const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16(o[2])) |
-                          (static_cast<uint32_t>(f32_to_bf16(o[3])) << 16);
+      const uint32_t w0 = pack_bf16x2(o[0], o[1]);
+      const uint32_t w1 = pack_bf16x2(o[2], o[3]);
       *reinterpret_cast<uint2*>(p.out + static_cast<int64_t>(tb0 + tt) * p.o_st + h * D + v0 +
                                 4 * g) = make_uint2(w0, w1);
     }
@@ -554,30 +567,28 @@ __device__ __forceinline__ void scan_chunk(const PrefillParams& p,
 // landed without waiting for the (independent) output stores.
 constexpr int VM_STORES_PER_CHUNK = 4;
 
-// Async copy of chunk jj's record and of this wave's value tile into buffer buf.
+// Async copy of chunk jj's record and of this wave's value tile into the LDS buffer
+// at byte address `lds`.
 template <int NW>
 __device__ __forceinline__ void copy_chunk_async(const PrefillParams& p,
                                                  const unsigned char* recbase, int cs, int ce,
                                                  int jj, int h, int v0, int w, int lane,
-                                                 unsigned char* buf, int vt_off) {
-  copy_record_async<NW>(recbase + static_cast<int64_t>(jj) * p.H * REC_BYTES, buf, w, lane);
+                                                 uint32_t lds, int vt_off) {
+  copy_record_async<NW>(uniform_addr(recbase + static_cast<int64_t>(jj) * p.H * REC_BYTES), lds, w,
+                        static_cast<uint32_t>(lane * 16));
   const int tbj = cs + jj * CHUNK;
-  copy_vtile_async(p, tbj, min(CHUNK, ce - tbj), h, v0, buf + vt_off, lane);
+  copy_vtile_async(p, tbj, min(CHUNK, ce - tbj), h, v0, lds + vt_off, lane);
 }
 
 // Chunk j: wait for its copy in `cur`, start chunk j+1's copy into `nxt`, compute chunk j.
-// `cur` and `nxt` are distinct LDS buffers; marking them __restrict__ tells the
-// compiler the reads of `cur` do not depend on the copy in flight into `nxt`.
 template <int NW>
 __device__ __forceinline__ void scan_step(const PrefillParams& p, const unsigned char* recbase,
-                                          int64_t rec_stride, int cs, int ce, int j, int nch,
-                                          int h, int v0, int w, int lane, int vt_off,
-                                          unsigned char* __restrict__ cur,
-                                          unsigned char* __restrict__ nxt, f32x4 (&S)[8]) {
-  (void)rec_stride;
+                                          int cs, int ce, int j, int nch, int h, int v0, int w,
+                                          int lane, int vt_off, const unsigned char* cur,
+                                          uint32_t cur_lds, uint32_t nxt_lds, f32x4 (&S)[8]) {
   if (j == 0) {
     // First chunk: copy it now and wait for it (nothing to overlap with yet).
-    copy_chunk_async<NW>(p, recbase, cs, ce, 0, h, v0, w, lane, cur, vt_off);
+    copy_chunk_async<NW>(p, recbase, cs, ce, 0, h, v0, w, lane, cur_lds, vt_off);
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   } else {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(VM_STORES_PER_CHUNK) : "memory");
@@ -585,20 +596,22 @@ __device__ __forceinline__ void scan_step(const PrefillParams& p, const unsigned
   // A bare barrier: __syncthreads() would also drain the output stores.
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-  if (j + 1 < nch) copy_chunk_async<NW>(p, recbase, cs, ce, j + 1, h, v0, w, lane, nxt, vt_off);
+  if (j + 1 < nch) copy_chunk_async<NW>(p, recbase, cs, ce, j + 1, h, v0, w, lane, nxt_lds, vt_off);
   scan_chunk(p, cur, cur + vt_off, cs + j * CHUNK, min(CHUNK, ce - cs - j * CHUNK), h, v0, lane,
              S);
 }
 
 template <int NW>
-__global__ __launch_bounds__(64 * NW) void prefill_scan_kernel(PrefillParams p) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void prefill_scan_kernel(PrefillParams p) {
   constexpr int BUF_BYTES = REC_BYTES + NW * VT_BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char srec0[BUF_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char srec1[BUF_BYTES];
   constexpr int BV = 16 * NW;
   constexpr int NVS = D / BV;
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, nl = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, nl = lane & 15, g = lane >> 4;
   // XCD-aware order: workgroup ids are dealt round-robin to the 8 XCDs (id % 8),
   // so the NVS value slices of one (sequence, head) pair get ids congruent mod 8
   // and share one L2 for the record they all read.
@@ -643,15 +656,14 @@ __global__ __launch_bounds__(64 * NW) void prefill_scan_kernel(PrefillParams p) 
   }
 
   const unsigned char* recbase = p.work + (slot0 * H + h) * REC_BYTES;
-  const int64_t rec_stride = static_cast<int64_t>(H) * REC_BYTES;
   const int vt_off = REC_BYTES + w * VT_BYTES;
   // Two chunks per trip so each half reads one fixed LDS buffer while the other
   // half's buffer is being filled.
+  const uint32_t lds0 = lds_addr(srec0), lds1 = lds_addr(srec1);
   for (int j = 0; j < nch; j += 2) {
-    scan_step<NW>(p, recbase, rec_stride, cs, ce, j, nch, h, v0, w, lane, vt_off, srec0, srec1, S);
+    scan_step<NW>(p, recbase, cs, ce, j, nch, h, v0, w, lane, vt_off, srec0, lds0, lds1, S);
     if (j + 1 >= nch) break;
-    scan_step<NW>(p, recbase, rec_stride, cs, ce, j + 1, nch, h, v0, w, lane, vt_off, srec1, srec0,
-                  S);
+    scan_step<NW>(p, recbase, cs, ce, j + 1, nch, h, v0, w, lane, vt_off, srec1, lds1, lds0, S);
   }
 
   if (p.final_state) {

@@ -165,10 +165,8 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p) {
     }
     if (rg == 0) {
       const float s = p.scale;
-      const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16(s * (yy.x + kq * u.x))) |
-                          (static_cast<uint32_t>(f32_to_bf16(s * (yy.y + kq * u.y))) << 16);
-      const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16(s * (yy.z + kq * u.z))) |
-                          (static_cast<uint32_t>(f32_to_bf16(s * (yy.w + kq * u.w))) << 16);
+      const uint32_t w0 = pack_bf16x2(s * (yy.x + kq * u.x), s * (yy.y + kq * u.y));
+      const uint32_t w1 = pack_bf16x2(s * (yy.z + kq * u.z), s * (yy.w + kq * u.w));
       uint16_t* o = p.out + (static_cast<int64_t>(b) * T + t) * p.o_st + h * D + v0 + 4 * cl;
       *reinterpret_cast<uint2*>(o) = make_uint2(w0, w1);
     }
