@@ -82,6 +82,120 @@ def cpu_baseline(case, tokens_per_seq):
                       f"fp64 numpy token loop, {os.cpu_count()} host CPUs visible)"}
 
 
+KERNEL_SOURCES = {
+    "kda_prefill_intra": "linear_attention_rule_amd/csrc/kda_prefill.hip",
+    "kda_prefill_scan": "linear_attention_rule_amd/csrc/kda_prefill.hip",
+    "kda_verify": "linear_attention_rule_amd/csrc/kda_verify.hip",
+}
+# rocprofv3 kernel names -> the names used in this benchmark.
+KERNEL_PATTERNS = {
+    "kda_prefill_intra": "prefill_intra_kernel",
+    "kda_prefill_scan": "prefill_scan_kernel",
+    "kda_verify": "verify_kernel",
+}
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+CALIB_BYTES = 1 << 30
+
+
+def source_hash(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for rel in (KERNEL_SOURCES[kernel], "linear_attention_rule_amd/csrc/kda_internal.h",
+                "linear_attention_rule_amd/build.py"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel, workload):
+    """Calibrated HBM bytes per launch from the committed counter runs, if still current."""
+    try:
+        with open(TRAFFIC_JSON) as f:
+            rec = json.load(f).get(f"{kernel}@{workload}")
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != source_hash(kernel):
+        return None
+    return rec["fetch_bytes"] + rec["write_bytes"]
+
+
+def summarize(prof_dirs, workload, out_md):
+    """Write a text summary of rocprofv3 CSV output (kernel trace, FETCH_SIZE and WRITE_SIZE
+    passes) for the KDA kernels, and record calibrated traffic in profiles/traffic.json."""
+    import csv
+    import glob
+    import re
+    stats = {}
+    counters = {}
+    calib = {}
+    for d in prof_dirs:
+        has_counters = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        for f in ([] if has_counters else
+                  glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)):
+            for r in csv.DictReader(open(f)):
+                for k, pat in KERNEL_PATTERNS.items():
+                    if pat in r["Kernel_Name"]:
+                        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+                        stats.setdefault(k, []).append(dur)
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                name, cname, val = r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])
+                if re.search(r"elementwise_kernel.*Mul", name):
+                    # the calibration copies (x * 1.0 over CALIB_BYTES) are the only such kernels
+                    calib.setdefault(cname, []).append(val)
+                for k, pat in KERNEL_PATTERNS.items():
+                    if pat in name:
+                        counters.setdefault(k, {}).setdefault(cname, []).append(val)
+    factors = {}
+    for cname in ("FETCH_SIZE", "WRITE_SIZE"):
+        big = [v for v in calib.get(cname, []) if v * 1024 > 0.5 * CALIB_BYTES]
+        factors[cname] = (CALIB_BYTES / 1024) / (sum(big) / len(big)) if big else None
+    lines = [f"# rocprofv3 summary: {workload}", "",
+             "Commands (run from /tmp with TMPDIR=/tmp; R = repository root):", "",
+             "    rocprofv3 --kernel-trace --stats --output-format csv -d OUT/prof_trace -o trace "
+             "-- python3 $R/bench.py --steps 20 --warmup 5 --no-cpu-baseline",
+             "    rocprofv3 --pmc FETCH_SIZE --kernel-trace --output-format csv -d OUT/prof_fetch "
+             "-o fetch -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline --calib-copy",
+             "    rocprofv3 --pmc WRITE_SIZE --kernel-trace --output-format csv -d OUT/prof_write "
+             "-o write -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline --calib-copy",
+             "    python3 $R/bench.py --summarize OUT/prof_trace OUT/prof_fetch OUT/prof_write "
+             "--summary-out <this file>", "",
+             "Kernel durations (kernel-trace run only):", "",
+             "| kernel | dispatches | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for k, v in sorted(stats.items()):
+        lines.append(f"| {k} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+    lines += ["", "Counter calibration (--calib-copy: an elementwise kernel reading and writing "
+              "1 GiB): bytes = counter KiB x 1024 x factor, with "
+              + ", ".join(f"{c} factor {f:.4f}" if f else f"{c}: not measured"
+                          for c, f in factors.items()), ""]
+    try:
+        with open(TRAFFIC_JSON) as f:
+            store = json.load(f)
+    except (OSError, ValueError):
+        store = {}
+    lines += ["| kernel | FETCH_SIZE KiB/dispatch (raw) | WRITE_SIZE KiB/dispatch (raw) | "
+              "calibrated HBM MB/dispatch |", "|---|---|---|---|"]
+    for k, cs in sorted(counters.items()):
+        fr = cs.get("FETCH_SIZE")
+        wr = cs.get("WRITE_SIZE")
+        if not fr or not wr:
+            continue
+        f_kib, w_kib = sum(fr) / len(fr), sum(wr) / len(wr)
+        ff, fw = factors["FETCH_SIZE"] or 1.0, factors["WRITE_SIZE"] or 1.0
+        fb, wb = f_kib * 1024 * ff, w_kib * 1024 * fw
+        lines.append(f"| {k} | {f_kib:.1f} | {w_kib:.1f} | {(fb + wb) / 1e6:.1f} |")
+        if factors["FETCH_SIZE"] and factors["WRITE_SIZE"]:
+            store[f"{k}@{workload}"] = {"fetch_bytes": fb, "write_bytes": wb,
+                                       "source_hash": source_hash(k),
+                                       "calibration": factors}
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(store, f, indent=1, sort_keys=True)
+    print("\n".join(lines))
+
+
 def roofline(bytes_, flops, seconds, bound="hbm"):
     if bound == "hbm":
         ach = bytes_ / seconds / 1e9
@@ -100,7 +214,16 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens per sequence in the oracle's timed sample")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run 1 GiB device copies (counter calibration under rocprofv3)")
+    ap.add_argument("--summarize", nargs="+", metavar="PROF_DIR",
+                    help="summarize rocprofv3 CSV output into --summary-out and exit")
+    ap.add_argument("--summary-out", default=None)
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize, f"prefill {W.LONG.name} + verify {W.VERIFY.name}",
+                  args.summary_out or os.path.join(ROOT, "profiles", "summary.md"))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); this build has no "
               "multi-GPU path", file=sys.stderr)
@@ -144,6 +267,16 @@ def main():
         verify()
         if ev is not None:
             ev[3].record()
+
+    if args.calib_copy:
+        # An elementwise kernel that reads 1 GiB and writes 1 GiB (a copy through the
+        # shader, unlike copy_, which may use the DMA engine and escape the counters).
+        src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -199,6 +332,9 @@ def main():
         "kda_prefill_scan": (s_scan, roofline(scan_bytes, 0, s_scan)),
         "kda_verify": (s_ver, roofline(verify_bytes, 0, s_ver)),
     }
+    workload = f"prefill {pcase.name} + verify {vcase.name}"
+    for k, (_, rl_k) in kernels.items():
+        rl_k["traffic"] = stored_traffic(k, workload)
     dom = max(kernels, key=lambda k: kernels[k][0])
     rl = dict(kernels[dom][1])
     rl["kernel"] = dom
@@ -223,7 +359,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"prefill {pcase.name} + verify {vcase.name}",
+            "workload": workload,
             "prefill": {"seqs": N, "seq_len": T // N, "heads": H, "head_dim": D, "chunk": 64,
                         "initial_state": "zero"},
             "verify": {"batch": B, "draft_steps": Tv, "heads": H, "pool_slots": vcase.pool_slots},
