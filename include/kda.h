@@ -107,6 +107,7 @@ size_t kda_chunk_prefill_workspace_size(int32_t num_seqs, int32_t total_tokens,
  *                   initial_state when both are indexed the same way.
  *   workspace       device scratch of at least kda_chunk_prefill_workspace_size bytes.
  * A zero-length sequence writes no output and copies its start state to final_state.
+ * (T_total/64 + N) * H above 2^31 - 1 chunk-heads returns KDA_ERR_UNSUPPORTED.
  */
 kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const void* g,
                              const void* beta_logits, const float* A_log, const float* dt_bias,

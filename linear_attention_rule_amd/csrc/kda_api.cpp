@@ -102,6 +102,9 @@ kda_status prefill_phases(const void* q, const void* k, const void* v, const voi
   if (N < 0 || T < 0 || H < 1)
     return fail(KDA_ERR_INVALID_ARGUMENT, "bad sizes N=%d T_total=%d H=%d", N, T, H);
   if (kda_status s = check_lower_bound(lower_bound)) return s;
+  if (kda::chunk_slots(N, T) * H > INT32_MAX)
+    return fail(KDA_ERR_UNSUPPORTED, "%lld chunk-heads exceed one launch",
+                static_cast<long long>(kda::chunk_slots(N, T) * H));
   if (!A_log || !dt_bias) return fail(KDA_ERR_INVALID_ARGUMENT, "A_log / dt_bias is NULL");
   if (N > 0 && !cu_seqlens) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL");
   if (T > 0 && (!q || !k || !v || !g || !beta_logits || !out))

@@ -71,6 +71,26 @@ __device__ __forceinline__ float row_scan16(float x) {
   return x;
 }
 
+// bf16 split of a pair: hi = RNE(a, b), lo = RNE of what hi leaves, both packed with the
+// low half holding a (the hardware pair conversion; a scalar bf16 cast is a multi-op
+// software sequence).
+__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = pack_bf16x2(a, b);
+  lo = pack_bf16x2(a - bf16lo_to_f32(hi), b - bf16hi_to_f32(hi));
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Workgroup barrier for LDS hand-offs only: waits for this wave's LDS operations, not
+// for its global stores (which nothing in the workgroup reads back).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ void load4_bf16(const uint16_t* p, float* dst) {
   const uint2 w = *reinterpret_cast<const uint2*>(p);
   dst[0] = bf16lo_to_f32(w.x);
@@ -128,7 +148,10 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
   __shared__ IntraSmem sm;
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, m = lane & 15, g = lane >> 4;
-  const int slot = blockIdx.x, h = blockIdx.y, H = p.H;
+  // Heads fastest: the H workgroups of one chunk slot run together, so their loads
+  // cover whole token rows and their records are contiguous.
+  const int H = p.H;
+  const int slot = blockIdx.x / H, h = blockIdx.x % H;
 
   // ---- a0: chunk map.  Sequence n owns slots [cu[n]/64 + n, ... + nchunks); find the
   // last n whose first slot is <= this one (binary search on device, no host sync).
@@ -153,16 +176,12 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
   const float vmask = valid ? 1.f : 0.f;
   const int64_t tok = static_cast<int64_t>(t0) + min(t, L - 1);
   float qv[32], kv[32], la[32];
+  float beta_t;
   {
-    float gv[32], dt[32];
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const float4 d4 = *reinterpret_cast<const float4*>(p.dt_bias + h * D + kperm(s, g, 4 * hh));
-        float* dd = dt + 8 * s + 4 * hh;
-        dd[0] = d4.x; dd[1] = d4.y; dd[2] = d4.z; dd[3] = d4.w;
-      }
+    // Every global load of the prologue is issued before the first is used (one
+    // memory round trip instead of the compiler's staggered two or three).
+    uint2 qr[8], kr[8], gr[8];
+    float4 dr[8];
     const uint16_t* qp = p.q + tok * p.q_st + h * D;
     const uint16_t* kp = p.k + tok * p.k_st + h * D;
     const uint16_t* gp = p.g + tok * p.g_st + h * D;
@@ -171,11 +190,30 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int c0 = kperm(s, g, 4 * hh);
-        load4_bf16(qp + c0, qv + 8 * s + 4 * hh);
-        load4_bf16(kp + c0, kv + 8 * s + 4 * hh);
-        load4_bf16(gp + c0, gv + 8 * s + 4 * hh);
+        qr[2 * s + hh] = *reinterpret_cast<const uint2*>(qp + c0);
+        kr[2 * s + hh] = *reinterpret_cast<const uint2*>(kp + c0);
+        gr[2 * s + hh] = *reinterpret_cast<const uint2*>(gp + c0);
+        dr[2 * s + hh] = *reinterpret_cast<const float4*>(p.dt_bias + h * D + c0);
       }
-    const float eA = __builtin_amdgcn_exp2f(p.A_log[h] * LOG2E);
+    const uint16_t braw = p.beta[tok * p.b_st + h];
+    const float alog = p.A_log[h];
+    asm volatile("" ::: "memory");
+    beta_t = vmask * sigmoid_f32(bf16_to_f32(braw));
+    float gv[32], dt[32];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float* qq = qv + 4 * j;
+      float* kk = kv + 4 * j;
+      float* gg = gv + 4 * j;
+      qq[0] = bf16lo_to_f32(qr[j].x); qq[1] = bf16hi_to_f32(qr[j].x);
+      qq[2] = bf16lo_to_f32(qr[j].y); qq[3] = bf16hi_to_f32(qr[j].y);
+      kk[0] = bf16lo_to_f32(kr[j].x); kk[1] = bf16hi_to_f32(kr[j].x);
+      kk[2] = bf16lo_to_f32(kr[j].y); kk[3] = bf16hi_to_f32(kr[j].y);
+      gg[0] = bf16lo_to_f32(gr[j].x); gg[1] = bf16hi_to_f32(gr[j].x);
+      gg[2] = bf16lo_to_f32(gr[j].y); gg[3] = bf16hi_to_f32(gr[j].y);
+      dt[4 * j] = dr[j].x; dt[4 * j + 1] = dr[j].y; dt[4 * j + 2] = dr[j].z; dt[4 * j + 3] = dr[j].w;
+    }
+    const float eA = __builtin_amdgcn_exp2f(alog * LOG2E);
     const float lbm = p.lb_log2e * vmask;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
@@ -196,7 +234,7 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
   ssk += __shfl_xor(ssk, 32);
   const float rq = __builtin_amdgcn_rsqf(ssq + L2_EPS);
   const float rk = __builtin_amdgcn_rsqf(ssk + L2_EPS);
-  if (g == 0) sm.beta[t] = vmask * sigmoid_f32(bf16_to_f32(p.beta[tok * p.b_st + h]));
+  if (g == 0) sm.beta[t] = beta_t;
 
   // In-block inclusive cumulative log2 decay (lanes m = 0..15 of a row are 16 tokens).
 #pragma unroll
@@ -207,7 +245,7 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
 #pragma unroll
       for (int e = 0; e < 8; ++e) sm.tot[w][kperm(s, g, e)] = la[8 * s + e];
   }
-  __syncthreads();
+  lds_barrier();
 
   // Per-channel tables from the four block sums (2 threads per channel).
   {
@@ -229,7 +267,7 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
           sm.Dsc[pair_idx(mm, ww)][c] = __builtin_amdgcn_exp2f(base[mm] - base[ww]);
     }
   }
-  __syncthreads();
+  lds_barrier();
   if (tid < 128) reinterpret_cast<float*>(rec + REC_GAMMA_OFF)[tid] = sm.Eb[4][tid];
 
   // ---- operands.  b = la (in-block cumulative), Lf = 2^b <= 1, Rf = 2^-b >= 1.
@@ -237,32 +275,55 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
   _Float16 kch[32];
   {
     const float rqs = rq * p.scale;
+    // Table entries of this thread's 32 channels: 16-byte LDS reads, all issued first.
+    float ebv[32], kcv[32];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const float4 e4 = *reinterpret_cast<const float4*>(&sm.Eb[w][kperm(s, g, 4 * hh)]);
+        const float4 c4 = *reinterpret_cast<const float4*>(&sm.KCb[w][kperm(s, g, 4 * hh)]);
+        float* ee = ebv + 8 * s + 4 * hh;
+        float* cc = kcv + 8 * s + 4 * hh;
+        ee[0] = e4.x; ee[1] = e4.y; ee[2] = e4.z; ee[3] = e4.w;
+        cc[0] = c4.x; cc[1] = c4.y; cc[2] = c4.z; cc[3] = c4.w;
+      }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       half8 kg, qg;
+      float klv[8], qlv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int i = 8 * s + e;
-        const int c = kperm(s, g, e);
         const float Lf = __builtin_amdgcn_exp2f(la[i]);
         const float Rf = __builtin_amdgcn_exp2f(-la[i]);
         const float kh = kv[i] * rk;
         const float qh = qv[i] * rq;
-        const float gam = sm.Eb[w][c] * Lf;
+        const float gam = ebv[i] * Lf;
         kg[e] = static_cast<_Float16>(-kh * gam);
         qg[e] = static_cast<_Float16>(qv[i] * rqs * gam);
-        kch[i] = static_cast<_Float16>(sm.KCb[w][c] * Rf * kh);
-        KL[s][e] = static_cast<__bf16>(kh * Lf);
-        const float ql = qh * Lf;
-        const __bf16 qlh = static_cast<__bf16>(ql);
-        QLh[s][e] = qlh;
-        QLl[s][e] = static_cast<__bf16>(ql - static_cast<float>(qlh));
-        const float r0 = kh * Rf;
-        const __bf16 r0h = static_cast<__bf16>(r0);
-        Rh[s][e] = r0h;
-        Rl[s][e] = static_cast<__bf16>(r0 - static_cast<float>(r0h));
-        kv[i] = r0;  // keep the fp32 right factor for publication
+        kch[i] = static_cast<_Float16>(kcv[i] * Rf * kh);
+        klv[e] = kh * Lf;
+        qlv[e] = qh * Lf;
+        kv[i] = kh * Rf;  // the fp32 right factor, kept for publication
       }
+      u32x4 klp, qhp, qlp, rhp, rlp;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        klp[j] = pack_bf16x2(klv[2 * j], klv[2 * j + 1]);
+        uint32_t hi, lo;
+        split_bf16x2(qlv[2 * j], qlv[2 * j + 1], hi, lo);
+        qhp[j] = hi;
+        qlp[j] = lo;
+        split_bf16x2(kv[8 * s + 2 * j], kv[8 * s + 2 * j + 1], hi, lo);
+        rhp[j] = hi;
+        rlp[j] = lo;
+      }
+      KL[s] = as_bf16x8(klp);
+      QLh[s] = as_bf16x8(qhp);
+      QLl[s] = as_bf16x8(qlp);
+      Rh[s] = as_bf16x8(rhp);
+      Rl[s] = as_bf16x8(rlp);
       *reinterpret_cast<half8*>(rec + (FR_KG + 4 * w + s) * 1024 + lane * 16) = kg;
       *reinterpret_cast<half8*>(rec + (FR_QG + 4 * w + s) * 1024 + lane * 16) = qg;
     }
@@ -276,32 +337,53 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
           make_float4(kv[8 * s + 4], kv[8 * s + 5], kv[8 * s + 6], kv[8 * s + 7]);
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- a2: G and P for row block w, column blocks 0..w (MFMA).
   for (int wb = 0; wb <= w; ++wb) {
     f32x4 accG = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+    bf16x8 bh[4], bl[4];
+    if (wb == w) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        bh[s] = Rh[s];
+        bl[s] = Rl[s];
+      }
+    } else {
+      // All of this block's LDS reads first (16-byte vectors), then the splits.
+      float4 sv[4][2], dv[4][2];
+      const float* dsc = sm.Dsc[pair_idx(w, wb)];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const float* src = sm.u.R0 + ((wb * 4 + s) * 64 + lane) * 8;
+        sv[s][0] = *reinterpret_cast<const float4*>(src);
+        sv[s][1] = *reinterpret_cast<const float4*>(src + 4);
+        dv[s][0] = *reinterpret_cast<const float4*>(dsc + kperm(s, g, 0));
+        dv[s][1] = *reinterpret_cast<const float4*>(dsc + kperm(s, g, 4));
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        u32x4 hp, lp;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          uint32_t hi, lo;
+          split_bf16x2(sv[s][q].x * dv[s][q].x, sv[s][q].y * dv[s][q].y, hi, lo);
+          hp[2 * q] = hi;
+          lp[2 * q] = lo;
+          split_bf16x2(sv[s][q].z * dv[s][q].z, sv[s][q].w * dv[s][q].w, hi, lo);
+          hp[2 * q + 1] = hi;
+          lp[2 * q + 1] = lo;
+        }
+        bh[s] = as_bf16x8(hp);
+        bl[s] = as_bf16x8(lp);
+      }
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      bf16x8 bh, bl;
-      if (wb == w) {
-        bh = Rh[s];
-        bl = Rl[s];
-      } else {
-        const float* src = sm.u.R0 + ((wb * 4 + s) * 64 + lane) * 8;
-        const float* dsc = sm.Dsc[pair_idx(w, wb)];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float r = src[e] * dsc[kperm(s, g, e)];
-          const __bf16 rh = static_cast<__bf16>(r);
-          bh[e] = rh;
-          bl[e] = static_cast<__bf16>(r - static_cast<float>(rh));
-        }
-      }
-      accG = mfma_bf16(KL[s], bh, accG);
-      accP = mfma_bf16(QLh[s], bh, accP);
-      accP = mfma_bf16(QLh[s], bl, accP);
-      accP = mfma_bf16(QLl[s], bh, accP);
+      accG = mfma_bf16(KL[s], bh[s], accG);
+      accP = mfma_bf16(QLh[s], bh[s], accP);
+      accP = mfma_bf16(QLh[s], bl[s], accP);
+      accP = mfma_bf16(QLl[s], bh[s], accP);
     }
     // lane (n, g) holds rows t = 16w + 4g + r, column i = 16wb + n
     const int i = 16 * wb + m;
@@ -325,7 +407,7 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
       sm.P[tr * ATS + i] = 0.f;
     }
   }
-  __syncthreads();   // R0 is dead from here on; the union's late view may be written
+  lds_barrier();   // R0 is dead from here on; the union's late view may be written
 
   // K_C transposed into LDS ([channel][token]) for the K_C^T fragments.
 #pragma unroll
@@ -354,7 +436,7 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
       for (int r = 0; r < 16; ++r) Tb[r * ATS + j] = x[r];
     }
   }
-  __syncthreads();
+  lds_barrier();
   // Off-diagonal blocks row by row: T_rc = -T_rr * sum_{j=c}^{r-1} A_rj T_jc, computed in
   // place (A_rc is last needed by T_rc itself; all reads of a row precede its writes).
   for (int rb = 1; rb < 4; ++rb) {
@@ -366,13 +448,13 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
                        ATS, acc, lane);
       store_tile(sm.u.late.tmp[cb], 16, acc, lane, 1.f);
     }
-    __syncthreads();
+    lds_barrier();
     if (cb < rb) {
       f32x4 z = {0.f, 0.f, 0.f, 0.f};
       z = mm16_lds(sm.AT + (16 * rb) * ATS + 16 * rb, ATS, sm.u.late.tmp[cb], 16, z, lane);
       store_tile(sm.AT + (16 * rb) * ATS + 16 * cb, ATS, z, lane, -1.f);
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   // ---- record fragments: T' = T diag(beta) and scale*tril(P) (row-major in LDS), K_C^T.
@@ -831,7 +913,7 @@ hipError_t launch_scan(const PrefillParams& p, hipStream_t s) {
 hipError_t launch_prefill(const PrefillParams& p, int phases, hipStream_t s) {
   if (p.N == 0) return hipSuccess;
   if ((phases & PHASE_INTRA) && p.num_slots_chunk > 0 && p.T_total > 0) {
-    const dim3 grid(static_cast<unsigned>(p.num_slots_chunk), static_cast<unsigned>(p.H));
+    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(p.num_slots_chunk) * p.H));
     hipLaunchKernelGGL(prefill_intra_kernel, grid, dim3(256), 0, s, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
