@@ -83,9 +83,11 @@ def cpu_baseline(case, tokens_per_seq):
 
 
 KERNEL_SOURCES = {
-    "kda_prefill_intra": "linear_attention_rule_amd/csrc/kda_prefill.hip",
-    "kda_prefill_scan": "linear_attention_rule_amd/csrc/kda_prefill.hip",
-    "kda_verify": "linear_attention_rule_amd/csrc/kda_verify.hip",
+    "kda_prefill_intra": ("linear_attention_rule_amd/csrc/kda_prefill_intra.hip",
+                          "linear_attention_rule_amd/csrc/kda_prefill_common.h"),
+    "kda_prefill_scan": ("linear_attention_rule_amd/csrc/kda_prefill_scan.hip",
+                         "linear_attention_rule_amd/csrc/kda_prefill_common.h"),
+    "kda_verify": ("linear_attention_rule_amd/csrc/kda_verify.hip",),
 }
 # rocprofv3 kernel names -> the names used in this benchmark.
 KERNEL_PATTERNS = {
@@ -100,7 +102,7 @@ CALIB_BYTES = 1 << 30
 def source_hash(kernel):
     import hashlib
     h = hashlib.sha256()
-    for rel in (KERNEL_SOURCES[kernel], "linear_attention_rule_amd/csrc/kda_internal.h",
+    for rel in (*KERNEL_SOURCES[kernel], "linear_attention_rule_amd/csrc/kda_internal.h",
                 "linear_attention_rule_amd/build.py"):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())

@@ -96,5 +96,7 @@ hipError_t launch_verify(const VerifyParams& p, hipStream_t s);
 constexpr int PHASE_INTRA = 1;
 constexpr int PHASE_SCAN = 2;
 hipError_t launch_prefill(const PrefillParams& p, int phases, hipStream_t s);
+// The intra-chunk kernel alone (called by launch_prefill).
+hipError_t launch_prefill_intra(const PrefillParams& p, hipStream_t s);
 
 }  // namespace kda
