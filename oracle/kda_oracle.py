@@ -27,6 +27,14 @@ What it computes (the plain definition, token by token, in float64):
   buffer; the pool stays read-only.  Reading used: row t holds the state after
   token t (0-based), so the last row is the all-accepted state.
 
+* Mixed speculative step and commit -- vLLM PR #55737, the "...code steps too"
+  commit message: outputs of the prefill segment and of the spec tokens are
+  scattered into one layer output by their token indices, and spec rows keep
+  the state their accepted tokens reached (num_accepted_tokens rollback).
+  Reading used: num_accepted counts the accepted tokens n of a row, so the
+  committed state is intermediate[b, n-1]; n = 0 (or more than T) commits
+  nothing.
+
 Readings taken where the pages are silent:
 L2 norm is x / sqrt(sum(x^2) + 1e-6); scale defaults to 1/sqrt(d_k); state
 layout is [K, V] (rows are key channels, the ones the gate decays); a
@@ -197,3 +205,45 @@ def recurrent_verify(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound,
         out[rows] = o.reshape(len(live), H, V)
         inter[live_arr, t] = S.reshape(len(live), H, K, V)
     return out, inter
+
+
+# ---------------------------------------------------------------------------
+# Mixed speculative step and commit (vLLM PR #55737, the "...code steps too"
+# commit message: in a step that carries both kinds of tokens the prefill
+# segment's outputs are scattered into the layer output by the non-spec token
+# indices and the spec tokens' outputs by the spec token indices; spec tokens
+# keep the recurrent kernel with num_accepted_tokens rollback).
+# ---------------------------------------------------------------------------
+
+def scatter_rows(values, index, num_rows, base=None):
+    """Row t of `values` placed at row index[t] of a [num_rows, ...] array.
+
+    Rows of `base` (zeros when None) that no index names are kept; an index
+    outside [0, num_rows) drops its row.  Indices are taken as distinct.
+    """
+    values = np.asarray(values)
+    out = (np.zeros((num_rows,) + values.shape[1:], dtype=values.dtype) if base is None
+           else np.array(base, copy=True))
+    for t, r in enumerate(np.asarray(index).reshape(-1)):
+        if 0 <= int(r) < num_rows:
+            out[int(r)] = values[t]
+    return out
+
+
+def commit_accepted(state_pool, intermediate, state_idx, num_accepted):
+    """Rollback commit after verify, returning the updated pool (a copy).
+
+    Row b accepted n = num_accepted[b] of its T draft tokens; its pool slot
+    state_idx[b] takes the state after those n tokens, intermediate[b, n-1].
+    Rows with a slot outside the pool, or n outside [1, T], change nothing.
+    """
+    pool = np.array(state_pool, copy=True)
+    inter = np.asarray(intermediate)
+    B, T = inter.shape[:2]
+    idx = np.asarray(state_idx).reshape(-1)
+    nacc = np.asarray(num_accepted).reshape(-1)
+    for b in range(B):
+        s, n = int(idx[b]), int(nacc[b])
+        if 0 <= s < pool.shape[0] and 1 <= n <= T:
+            pool[s] = inter[b, n - 1]
+    return pool
