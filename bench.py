@@ -35,7 +35,8 @@ import torch
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from linear_attention_rule_amd import chunk_prefill, prefill_workspace_bytes, recurrent_verify  # noqa: E402
+from linear_attention_rule_amd import (chunk_prefill, commit_accepted,  # noqa: E402
+                                       prefill_workspace_bytes, recurrent_verify)
 from linear_attention_rule_amd import workloads as W  # noqa: E402
 
 METRIC = "KDA prefill µs/layer & tokens/s (8192x4, H=16, d=128); verify µs/layer"
@@ -88,12 +89,14 @@ KERNEL_SOURCES = {
     "kda_prefill_scan": ("linear_attention_rule_amd/csrc/kda_prefill_scan.hip",
                          "linear_attention_rule_amd/csrc/kda_prefill_common.h"),
     "kda_verify": ("linear_attention_rule_amd/csrc/kda_verify.hip",),
+    "kda_commit": ("linear_attention_rule_amd/csrc/kda_commit.hip",),
 }
 # rocprofv3 kernel names -> the names used in this benchmark.
 KERNEL_PATTERNS = {
     "kda_prefill_intra": "prefill_intra_kernel",
     "kda_prefill_scan": "prefill_scan_kernel",
     "kda_verify": "verify_kernel",
+    "kda_commit": "commit_kernel",
 }
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 CALIB_BYTES = 1 << 30
@@ -121,7 +124,11 @@ def stored_traffic(kernel, workload):
     return rec["fetch_bytes"] + rec["write_bytes"]
 
 
-def summarize(prof_dirs, workload, out_md):
+MAIN_WORKLOAD = f"prefill {W.LONG.name} + verify {W.VERIFY.name}"
+EXTRAS_WORKLOAD = f"commit after {W.VERIFY.name} + mixed step {W.MIXED.name}"
+
+
+def summarize(prof_dirs, workload, out_md, mode_flag):
     """Write a text summary of rocprofv3 CSV output (kernel trace, FETCH_SIZE and WRITE_SIZE
     passes) for the KDA kernels, and record calibrated traffic in profiles/traffic.json."""
     import csv
@@ -155,13 +162,15 @@ def summarize(prof_dirs, workload, out_md):
     lines = [f"# rocprofv3 summary: {workload}", "",
              "Commands (run from /tmp with TMPDIR=/tmp; R = repository root):", "",
              "    rocprofv3 --kernel-trace --stats --output-format csv -d OUT/prof_trace -o trace "
-             "-- python3 $R/bench.py --steps 20 --warmup 5 --no-cpu-baseline",
+             f"-- python3 $R/bench.py --steps 20 --warmup 5 --no-cpu-baseline {mode_flag}",
              "    rocprofv3 --pmc FETCH_SIZE --kernel-trace --output-format csv -d OUT/prof_fetch "
-             "-o fetch -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline --calib-copy",
+             f"-o fetch -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline {mode_flag} "
+             "--calib-copy",
              "    rocprofv3 --pmc WRITE_SIZE --kernel-trace --output-format csv -d OUT/prof_write "
-             "-o write -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline --calib-copy",
+             f"-o write -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline {mode_flag} "
+             "--calib-copy",
              "    python3 $R/bench.py --summarize OUT/prof_trace OUT/prof_fetch OUT/prof_write "
-             "--summary-out <this file>", "",
+             f"{mode_flag} --summary-out <this file>", "",
              "Kernel durations (kernel-trace run only):", "",
              "| kernel | dispatches | avg us | min us | max us |", "|---|---|---|---|---|"]
     for k, v in sorted(stats.items()):
@@ -208,6 +217,80 @@ def roofline(bytes_, flops, seconds, bound="hbm"):
             "frac": round(ach / MFMA_BF16_PEAK_TFS, 4), "traffic": None}
 
 
+def calibration_copies():
+    """An elementwise kernel that reads 1 GiB and writes 1 GiB (a copy through the shader,
+    unlike copy_, which may use the DMA engine and escape the counters)."""
+    src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+
+
+def time_calls(fn, iters, warmup=3):
+    """Mean seconds per call of fn, by HIP events on torch's current stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / iters
+
+
+def bench_next_rows(iters):
+    """The rows after the hot path: the rollback commit at the verify size, and one mixed
+    speculative step (prefill segment and spec rows scattered into one layer output)."""
+    vcase = W.VERIFY
+    B, Tv, H = vcase.batch, vcase.steps, vcase.heads
+    rng = np.random.default_rng(4000)
+    inter = torch.full((B, Tv, H, D, D), 0.5, dtype=torch.float32, device="cuda")
+    pool = torch.zeros((vcase.pool_slots, H, D, D), dtype=torch.float32, device="cuda")
+    idx = torch.from_numpy(rng.permutation(vcase.pool_slots)[:B].astype(np.int32)).cuda()
+    nacc = torch.from_numpy(rng.integers(1, Tv + 1, size=B).astype(np.int32)).cuda()
+    t_commit = time_calls(lambda: commit_accepted(inter, idx, nacc, pool), iters)
+    commit_bytes = B * H * 2 * STATE_BYTES + 2 * B * 4
+    del inter, pool
+
+    m = W.make_mixed(W.MIXED)
+    pre, spec = to_dev(m["prefill"]), to_dev(m["spec"])
+    Tp, Hm = pre["q"].shape[0], pre["q"].shape[1]
+    Np = pre["cu_seqlens"].numel() - 1
+    Bs, Ts = W.MIXED.spec.batch, W.MIXED.spec.steps
+    core = torch.empty((m["out_rows"], Hm, D), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(prefill_workspace_bytes(Np, Tp, Hm), dtype=torch.uint8, device="cuda")
+    fin = torch.empty((Np, Hm, D, D), dtype=torch.float32, device="cuda")
+    sinter = torch.empty((Bs, Ts, Hm, D, D), dtype=torch.float32, device="cuda")
+    ns_idx, sp_idx = m["non_spec_idx"].cuda(), m["spec_idx"].cuda()
+
+    def mixed():
+        chunk_prefill(pre["q"], pre["k"], pre["v"], pre["g"], pre["beta_logits"], pre["A_log"],
+                      pre["dt_bias"], pre["lower_bound"], pre["cu_seqlens"], out=core,
+                      final_state=fin, workspace=ws, scale=pre["scale"], out_token_index=ns_idx)
+        recurrent_verify(spec["q"], spec["k"], spec["v"], spec["g"], spec["beta_logits"],
+                         spec["A_log"], spec["dt_bias"], spec["lower_bound"], spec["state_pool"],
+                         spec["state_idx"], Ts, intermediate=sinter, out=core, scale=spec["scale"],
+                         out_token_index=sp_idx)
+
+    t_mixed = time_calls(mixed, iters)
+    tokens = Tp + Bs * Ts
+    mixed_bytes = (tokens * Hm * BYTES_PER_TOKEN_HEAD + Np * Hm * STATE_BYTES
+                   + Bs * Hm * STATE_BYTES * (1 + Ts))
+    rl_commit = roofline(commit_bytes, 0, t_commit)
+    rl_commit["traffic"] = stored_traffic("kda_commit", EXTRAS_WORKLOAD)
+    return {
+        "commit": {"workload": f"commit after {vcase.name}", "us": round(t_commit * 1e6, 2),
+                   "roofline": rl_commit, "algorithmic_bytes": commit_bytes},
+        "mixed_step": {"workload": W.MIXED.name, "us": round(t_mixed * 1e6, 2),
+                       "tokens_per_s": round(tokens / t_mixed, 1),
+                       "roofline": roofline(mixed_bytes, 0, t_mixed),
+                       "algorithmic_bytes": mixed_bytes},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -221,10 +304,16 @@ def main():
     ap.add_argument("--summarize", nargs="+", metavar="PROF_DIR",
                     help="summarize rocprofv3 CSV output into --summary-out and exit")
     ap.add_argument("--summary-out", default=None)
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the commit and mixed-step measurements")
+    ap.add_argument("--extras-only", action="store_true",
+                    help="measure only the commit and the mixed step (one JSON line)")
     args = ap.parse_args()
     if args.summarize:
-        summarize(args.summarize, f"prefill {W.LONG.name} + verify {W.VERIFY.name}",
-                  args.summary_out or os.path.join(ROOT, "profiles", "summary.md"))
+        extras = args.extras_only
+        summarize(args.summarize, EXTRAS_WORKLOAD if extras else MAIN_WORKLOAD,
+                  args.summary_out or os.path.join(ROOT, "profiles", "summary.md"),
+                  "--extras-only" if extras else "--no-extras")
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); this build has no "
@@ -233,6 +322,12 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+
+    if args.calib_copy:
+        calibration_copies()
+    if args.extras_only:
+        print(json.dumps({"next_rows": bench_next_rows(args.steps)}), flush=True)
+        return
 
     pcase, vcase = W.LONG, W.VERIFY
     log(f"generating {pcase.name} and {vcase.name}")
@@ -270,15 +365,6 @@ def main():
         if ev is not None:
             ev[3].record()
 
-    if args.calib_copy:
-        # An elementwise kernel that reads 1 GiB and writes 1 GiB (a copy through the
-        # shader, unlike copy_, which may use the DMA engine and escape the counters).
-        src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -334,7 +420,7 @@ def main():
         "kda_prefill_scan": (s_scan, roofline(scan_bytes, 0, s_scan)),
         "kda_verify": (s_ver, roofline(verify_bytes, 0, s_ver)),
     }
-    workload = f"prefill {pcase.name} + verify {vcase.name}"
+    workload = MAIN_WORKLOAD
     for k, (_, rl_k) in kernels.items():
         rl_k["traffic"] = stored_traffic(k, workload)
     dom = max(kernels, key=lambda k: kernels[k][0])
@@ -345,6 +431,10 @@ def main():
     if not args.no_cpu_baseline:
         log(f"oracle baseline on {args.cpu_tokens} tokens/sequence")
         cpu = cpu_baseline(pcase, args.cpu_tokens)
+
+    extras = None if args.no_extras else bench_next_rows(args.steps)
+    if extras:
+        log(f"commit {extras['commit']['us']} us  mixed step {extras['mixed_step']['us']} us")
 
     value = T / s_prefill
     res = {
@@ -386,6 +476,7 @@ def main():
                                        prefill_flops / (MFMA_BF16_PEAK_TFS * 1e12)) / s_prefill, 4),
         },
         "cpu_baseline": cpu,
+        "next_rows": extras,
         "context": {"flashkda_gb300_us_per_layer_8192x4": 146,
                     "note": "the pages' number, other hardware; not a target"},
     }

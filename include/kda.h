@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 #define KDA_HEAD_DIM 128
 #define KDA_MAX_VERIFY_STEPS 64
 
@@ -69,6 +69,14 @@ typedef struct kda_prefill_desc {
   int64_t q_token_stride, k_token_stride, v_token_stride, g_token_stride;  /* elements, 0 = H*128 */
   int64_t beta_token_stride; /* elements, 0 = H */
   int64_t out_token_stride;  /* elements, 0 = H*128 */
+  /* Scattered output (the mixed speculative step of vLLM PR #55737, "...code steps
+   * too" commit: prefill outputs land in the layer buffer at non_spec_token_indx).
+   * NULL: token t's output is row t of out.  Otherwise a device int32 [T_total]:
+   * token t's output is row out_token_index[t] of out (rows out_token_stride
+   * apart); an index outside [0, out_rows) is not written.  Indices must be
+   * distinct (rows written twice hold either value). */
+  const int32_t* out_token_index;
+  int64_t out_rows;          /* rows of out when out_token_index is given */
 } kda_prefill_desc;
 
 typedef struct kda_verify_desc {
@@ -81,7 +89,18 @@ typedef struct kda_verify_desc {
   int64_t q_token_stride, k_token_stride, v_token_stride, g_token_stride;
   int64_t beta_token_stride;
   int64_t out_token_stride;
+  /* As in kda_prefill_desc, for token b*num_steps + t (spec_token_indx). */
+  const int32_t* out_token_index;
+  int64_t out_rows;
 } kda_verify_desc;
+
+typedef struct kda_commit_desc {
+  int32_t batch;             /* B verify rows */
+  int32_t num_steps;         /* T: rows per verify row in intermediate_state */
+  int32_t num_heads;         /* H */
+  int32_t head_dim;          /* must be 128 */
+  int32_t num_slots;         /* rows of state_pool */
+} kda_commit_desc;
 
 /* Bytes of caller-provided workspace kda_chunk_prefill needs for these shapes.
  * Returns 0 for shapes the library does not support. */
@@ -162,6 +181,24 @@ kda_status kda_recurrent_verify(const void* q, const void* k, const void* v, con
                                 float lower_bound, const float* state_pool,
                                 const int32_t* state_idx, float* intermediate_state, void* out,
                                 const kda_verify_desc* desc, void* stream);
+
+/*
+ * Commit after verify: the num_accepted_tokens rollback of vLLM PR #55737
+ * ("...code steps too" commit message: spec-decode tokens keep the recurrent
+ * kernel with num_accepted_tokens rollback).  For each row b whose slot
+ * s = state_idx[b] lies in [0, num_slots) and whose count n = num_accepted[b]
+ * lies in [1, T], state_pool[s] (all heads) becomes intermediate_state[b, n-1],
+ * the state after the n accepted tokens.  Other rows leave the pool unchanged.
+ *   intermediate_state  fp32 [B, T, H, 128, 128] as written by kda_recurrent_verify;
+ *                       must not overlap the pool
+ *   state_idx           device int32 [B] (the verify call's indices)
+ *   num_accepted        device int32 [B]
+ *   state_pool          fp32 [num_slots, H, 128, 128], updated in place
+ * Rows of one call must name distinct slots.
+ */
+kda_status kda_commit_accepted(const float* intermediate_state, const int32_t* state_idx,
+                               const int32_t* num_accepted, float* state_pool,
+                               const kda_commit_desc* desc, void* stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* kda_last_error(void);

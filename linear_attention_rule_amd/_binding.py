@@ -32,7 +32,8 @@ class PrefillDesc(ctypes.Structure):
                 ("scale", ctypes.c_float), ("num_state_rows", ctypes.c_int32),
                 ("q_token_stride", ctypes.c_int64), ("k_token_stride", ctypes.c_int64),
                 ("v_token_stride", ctypes.c_int64), ("g_token_stride", ctypes.c_int64),
-                ("beta_token_stride", ctypes.c_int64), ("out_token_stride", ctypes.c_int64)]
+                ("beta_token_stride", ctypes.c_int64), ("out_token_stride", ctypes.c_int64),
+                ("out_token_index", ctypes.c_void_p), ("out_rows", ctypes.c_int64)]
 
 
 class VerifyDesc(ctypes.Structure):
@@ -41,9 +42,17 @@ class VerifyDesc(ctypes.Structure):
                 ("scale", ctypes.c_float), ("num_slots", ctypes.c_int32),
                 ("q_token_stride", ctypes.c_int64), ("k_token_stride", ctypes.c_int64),
                 ("v_token_stride", ctypes.c_int64), ("g_token_stride", ctypes.c_int64),
-                ("beta_token_stride", ctypes.c_int64), ("out_token_stride", ctypes.c_int64)]
+                ("beta_token_stride", ctypes.c_int64), ("out_token_stride", ctypes.c_int64),
+                ("out_token_index", ctypes.c_void_p), ("out_rows", ctypes.c_int64)]
 
 
+class CommitDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_steps", ctypes.c_int32),
+                ("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("num_slots", ctypes.c_int32)]
+
+
+ABI_VERSION = 2
 _lib = None
 
 
@@ -78,8 +87,11 @@ def load_library(path: str | None = None):
     lib.kda_recurrent_verify.restype = ctypes.c_int
     lib.kda_recurrent_verify.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp,
                                          ctypes.POINTER(VerifyDesc), vp]
-    if lib.kda_abi_version() != 1:
-        raise RuntimeError("libkda ABI version mismatch")
+    lib.kda_commit_accepted.restype = ctypes.c_int
+    lib.kda_commit_accepted.argtypes = [vp, vp, vp, vp, ctypes.POINTER(CommitDesc), vp]
+    if lib.kda_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"libkda ABI version {lib.kda_abi_version()}, binding expects "
+                           f"{ABI_VERSION}")
     _lib = lib
     return lib
 
@@ -148,15 +160,30 @@ def prefill_workspace_bytes(num_seqs: int, total_tokens: int, num_heads: int) ->
     return int(lib.kda_chunk_prefill_workspace_size(num_seqs, total_tokens, num_heads, HEAD_DIM))
 
 
+def _out_index(out, out_token_index, tokens, H):
+    """Validates out against an optional scatter index; returns (token stride, rows, ptr)."""
+    os_ = _token_tensor("out", out, H, HEAD_DIM)
+    if out_token_index is None:
+        if out.shape[0] != tokens:
+            raise ValueError(f"out must have {tokens} tokens")
+        return os_, 0, None
+    _i32("out_token_index", out_token_index, tokens)
+    return os_, int(out.shape[0]), _ptr(out_token_index)
+
+
 def chunk_prefill(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, cu_seqlens, *,
                   initial_state=None, initial_state_idx=None, out=None, final_state=None,
                   write_final_state=True, scale=None, workspace=None, check=False,
-                  phase="both"):
+                  phase="both", out_token_index=None):
     """Varlen chunked KDA prefill.  Returns (out, final_state or None).
 
     phase: "both" (kda_chunk_prefill), or "intra" / "scan" for the two halves of
     the same call (kda_chunk_prefill_intra / kda_chunk_prefill_scan), which must
     then be given the same workspace.
+
+    out_token_index: optional int32 [T] on the device; token t's output goes to row
+    out_token_index[t] of `out` (which must then be given: the layer buffer), rows
+    outside [0, out.shape[0]) are not written.
 
     q, k, v, g: bf16 [T, H, 128] (token stride free, heads dense); beta_logits bf16 [T, H];
     A_log f32 [H]; dt_bias f32 [H, 128]; cu_seqlens int32 [N+1] on the device.
@@ -188,10 +215,10 @@ def chunk_prefill(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, cu_seqle
     if initial_state_idx is not None:
         _i32("initial_state_idx", initial_state_idx, N)
     if out is None:
+        if out_token_index is not None:
+            raise ValueError("out_token_index needs the destination buffer `out`")
         out = torch.empty((T, H, HEAD_DIM), dtype=torch.bfloat16, device=dev)
-    os_ = _token_tensor("out", out, H, HEAD_DIM)
-    if out.shape[0] != T:
-        raise ValueError("out must have T tokens")
+    os_, out_rows, oidx = _out_index(out, out_token_index, T, H)
     if final_state is None and write_final_state:
         final_state = torch.empty((N, H, HEAD_DIM, HEAD_DIM), dtype=torch.float32, device=dev)
     if final_state is not None:
@@ -204,7 +231,7 @@ def chunk_prefill(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, cu_seqle
         if int(cu[0]) != 0 or int(cu[-1]) != T or bool((cu[1:] < cu[:-1]).any()):
             raise ValueError("cu_seqlens must start at 0, be non-decreasing and end at T")
     desc = PrefillDesc(N, T, H, HEAD_DIM, float(scale) if scale else 0.0, rows,
-                       qs, ks, vs, gs, bs, os_)
+                       qs, ks, vs, gs, bs, os_, oidx, out_rows)
     fn = {"both": lib.kda_chunk_prefill, "intra": lib.kda_chunk_prefill_intra,
           "scan": lib.kda_chunk_prefill_scan}[phase]
     st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta_logits), _ptr(A_log),
@@ -218,8 +245,11 @@ def chunk_prefill(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, cu_seqle
 
 
 def recurrent_verify(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, state_pool, state_idx,
-                     num_steps, *, intermediate=None, out=None, scale=None):
-    """Fused multi-step verify.  Returns (out [B*T, H, 128] bf16, intermediate [B, T, H, 128, 128] f32)."""
+                     num_steps, *, intermediate=None, out=None, scale=None, out_token_index=None):
+    """Fused multi-step verify.  Returns (out [B*T, H, 128] bf16, intermediate [B, T, H, 128, 128] f32).
+
+    out_token_index: as in chunk_prefill, for token b*T + t.
+    """
     lib = load_library()
     BT, H = int(q.shape[0]), int(q.shape[1])
     T = int(num_steps)
@@ -238,19 +268,42 @@ def recurrent_verify(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, state
     _i32("state_idx", state_idx, B)
     dev = q.device
     if out is None:
+        if out_token_index is not None:
+            raise ValueError("out_token_index needs the destination buffer `out`")
         out = torch.empty((BT, H, HEAD_DIM), dtype=torch.bfloat16, device=dev)
-    os_ = _token_tensor("out", out, H, HEAD_DIM)
+    os_, out_rows, oidx = _out_index(out, out_token_index, BT, H)
     if intermediate is None:
         intermediate = torch.empty((B, T, H, HEAD_DIM, HEAD_DIM), dtype=torch.float32, device=dev)
     _f32("intermediate", intermediate, (B, T, H, HEAD_DIM, HEAD_DIM))
     desc = VerifyDesc(B, T, H, HEAD_DIM, float(scale) if scale else 0.0, slots,
-                      qs, ks, vs, gs, bs, os_)
+                      qs, ks, vs, gs, bs, os_, oidx, out_rows)
     st = lib.kda_recurrent_verify(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta_logits),
                                   _ptr(A_log), _ptr(dt_bias), float(lower_bound), _ptr(state_pool),
                                   _ptr(state_idx), _ptr(intermediate), _ptr(out),
                                   ctypes.byref(desc), _stream_handle(dev))
     _check(st)
     return out, intermediate
+
+
+def commit_accepted(intermediate, state_idx, num_accepted, state_pool):
+    """Rollback commit after verify: state_pool[state_idx[b]] <- intermediate[b, num_accepted[b]-1]
+    for rows with an in-range slot and 1 <= num_accepted[b] <= T.  Updates state_pool in place
+    and returns it."""
+    lib = load_library()
+    if intermediate.dim() != 5:
+        raise ValueError("intermediate must be [B, T, H, 128, 128]")
+    B, T, H = (int(x) for x in intermediate.shape[:3])
+    _f32("intermediate", intermediate, (B, T, H, HEAD_DIM, HEAD_DIM))
+    slots = int(state_pool.shape[0])
+    _f32("state_pool", state_pool, (slots, H, HEAD_DIM, HEAD_DIM))
+    _i32("state_idx", state_idx, B)
+    _i32("num_accepted", num_accepted, B)
+    desc = CommitDesc(B, T, H, HEAD_DIM, slots)
+    st = lib.kda_commit_accepted(_ptr(intermediate), _ptr(state_idx), _ptr(num_accepted),
+                                 _ptr(state_pool), ctypes.byref(desc),
+                                 _stream_handle(intermediate.device))
+    _check(st)
+    return state_pool
 
 
 def default_scale() -> float:

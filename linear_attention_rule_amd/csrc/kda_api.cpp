@@ -60,6 +60,21 @@ kda_status check_stride(const char* name, int64_t stride, int64_t dense, int64_t
   return KDA_OK;
 }
 
+// Output rows reachable through an optional scatter index (tokens rows when none).
+kda_status check_out_index(const int32_t* idx, int64_t rows, int64_t tokens, int64_t* out_rows) {
+  if (!idx) {
+    *out_rows = tokens;
+    return KDA_OK;
+  }
+  if (rows < 0 || rows > INT32_MAX)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "out_rows %lld outside [0, 2^31)",
+                static_cast<long long>(rows));
+  if (tokens > 0 && (reinterpret_cast<uintptr_t>(idx) & 3u))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "out_token_index must be 4-byte aligned");
+  *out_rows = rows;
+  return KDA_OK;
+}
+
 kda_status check_lower_bound(float lb) {
   if (!std::isfinite(lb)) return fail(KDA_ERR_UNSUPPORTED, "lower_bound must be finite");
   // The intra-chunk factorisation keeps every exponential of a 16-token block
@@ -121,12 +136,16 @@ kda_status prefill_phases(const void* q, const void* k, const void* v, const voi
   if (kda_status s = check_stride("g", desc->g_token_stride, HD, HD, &gs)) return s;
   if (kda_status s = check_stride("beta_logits", desc->beta_token_stride, H, H, &bs)) return s;
   if (kda_status s = check_stride("out", desc->out_token_stride, HD, HD, &os)) return s;
+  int64_t orows;
+  if (kda_status s = check_out_index(desc->out_token_index, desc->out_rows, T, &orows)) return s;
   if (T > 0) {
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(out))
       return fail(KDA_ERR_INVALID_ARGUMENT, "q/k/v/g/out must be 16-byte aligned");
     if ((qs | ks | vs | gs | os) & 7)
       return fail(KDA_ERR_INVALID_ARGUMENT, "q/k/v/g/out token strides must be multiples of 8");
-    const Span so = span_of(out, T, os, HD, 2);
+    const Span so = span_of(out, orows, os, HD, 2);
+    if (desc->out_token_index && overlaps(so, span_of(desc->out_token_index, T, 1, 1, 4)))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "out overlaps out_token_index");
     const void* ins[4] = {q, k, v, g};
     const int64_t sts[4] = {qs, ks, vs, gs};
     for (int i = 0; i < 4; ++i)
@@ -157,6 +176,8 @@ kda_status prefill_phases(const void* q, const void* k, const void* v, const voi
   p.init = initial_state;
   p.init_idx = initial_state_idx;
   p.out = static_cast<uint16_t*>(out);
+  p.out_idx = desc->out_token_index;
+  p.out_rows = orows;
   p.final_state = final_state;
   p.work = static_cast<unsigned char*>(workspace);
   p.lb_log2e = lower_bound * kda::LOG2E;
@@ -222,6 +243,10 @@ kda_status kda_recurrent_verify(const void* q, const void* k, const void* v, con
   if (kda_status s = check_stride("g", desc->g_token_stride, HD, HD, &gs)) return s;
   if (kda_status s = check_stride("beta_logits", desc->beta_token_stride, H, H, &bs)) return s;
   if (kda_status s = check_stride("out", desc->out_token_stride, HD, HD, &os)) return s;
+  int64_t orows;
+  if (kda_status s = check_out_index(desc->out_token_index, desc->out_rows,
+                                     static_cast<int64_t>(B) * T, &orows))
+    return s;
   if (B == 0) return ok();
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(out) ||
       !aligned16(state_pool) || !aligned16(intermediate_state) || !aligned16(dt_bias))
@@ -234,7 +259,9 @@ kda_status kda_recurrent_verify(const void* q, const void* k, const void* v, con
   const Span s_int = span_of(intermediate_state, BT, H * state_elems, H * state_elems, 4);
   if (overlaps(s_pool, s_int))
     return fail(KDA_ERR_INVALID_ARGUMENT, "intermediate_state overlaps state_pool");
-  const Span so = span_of(out, BT, os, HD, 2);
+  const Span so = span_of(out, orows, os, HD, 2);
+  if (desc->out_token_index && overlaps(so, span_of(desc->out_token_index, BT, 1, 1, 4)))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "out overlaps out_token_index");
   const void* ins[4] = {q, k, v, g};
   const int64_t sts[4] = {qs, ks, vs, gs};
   for (int i = 0; i < 4; ++i)
@@ -255,6 +282,8 @@ kda_status kda_recurrent_verify(const void* q, const void* k, const void* v, con
   p.idx = state_idx;
   p.inter = intermediate_state;
   p.out = static_cast<uint16_t*>(out);
+  p.out_idx = desc->out_token_index;
+  p.out_rows = orows;
   p.lb_log2e = lower_bound * kda::LOG2E;
   p.scale = desc->scale > 0.f ? desc->scale : 1.0f / std::sqrt(static_cast<float>(KDA_HEAD_DIM));
   p.B = B;
@@ -264,6 +293,46 @@ kda_status kda_recurrent_verify(const void* q, const void* k, const void* v, con
   p.q_st = qs; p.k_st = ks; p.v_st = vs; p.g_st = gs; p.b_st = bs; p.o_st = os;
   const hipError_t e = kda::launch_verify(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "verify launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+kda_status kda_commit_accepted(const float* intermediate_state, const int32_t* state_idx,
+                               const int32_t* num_accepted, float* state_pool,
+                               const kda_commit_desc* desc, void* stream) {
+  if (!desc) return fail(KDA_ERR_INVALID_ARGUMENT, "desc is NULL");
+  const int B = desc->batch, T = desc->num_steps, H = desc->num_heads;
+  if (desc->head_dim != KDA_HEAD_DIM)
+    return fail(KDA_ERR_UNSUPPORTED, "head_dim %d unsupported (only 128)", desc->head_dim);
+  if (B < 0 || T < 1 || H < 1 || desc->num_slots < 1)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "bad sizes B=%d T=%d H=%d slots=%d", B, T, H,
+                desc->num_slots);
+  if (B == 0) return ok();
+  if (!intermediate_state || !state_idx || !num_accepted || !state_pool)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "a pointer is NULL");
+  if (!aligned16(intermediate_state) || !aligned16(state_pool))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "state buffers must be 16-byte aligned");
+  if (static_cast<int64_t>(B) * H > INT32_MAX)
+    return fail(KDA_ERR_UNSUPPORTED, "B*H exceeds one launch");
+  const int64_t state_elems = static_cast<int64_t>(KDA_HEAD_DIM) * KDA_HEAD_DIM;
+  const Span s_pool = span_of(state_pool, desc->num_slots, H * state_elems, H * state_elems, 4);
+  const Span s_int = span_of(intermediate_state, static_cast<int64_t>(B) * T, H * state_elems,
+                             H * state_elems, 4);
+  if (overlaps(s_pool, s_int))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "intermediate_state overlaps state_pool");
+  if (overlaps(s_pool, span_of(state_idx, B, 1, 1, 4)) ||
+      overlaps(s_pool, span_of(num_accepted, B, 1, 1, 4)))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "state_pool overlaps an index array");
+  kda::CommitParams p{};
+  p.inter = intermediate_state;
+  p.idx = state_idx;
+  p.n_acc = num_accepted;
+  p.pool = state_pool;
+  p.B = B;
+  p.T = T;
+  p.H = H;
+  p.slots = desc->num_slots;
+  const hipError_t e = kda::launch_commit(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "commit launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

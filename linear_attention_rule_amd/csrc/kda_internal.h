@@ -51,10 +51,20 @@ struct VerifyParams {
   const int32_t* idx;
   float* inter;
   uint16_t* out;
+  const int32_t* out_idx;  // output row of each token, or null (row = token)
+  int64_t out_rows;        // rows of out addressable through out_idx
   float lb_log2e;      // lower_bound * log2(e): gate computed in log2 units
   float scale;
   int B, T, H, slots;
   int64_t q_st, k_st, v_st, g_st, b_st, o_st;
+};
+
+struct CommitParams {
+  const float* inter;
+  const int32_t* idx;
+  const int32_t* n_acc;
+  float* pool;
+  int B, T, H, slots;
 };
 
 struct PrefillParams {
@@ -69,6 +79,8 @@ struct PrefillParams {
   const float* init;
   const int32_t* init_idx;
   uint16_t* out;
+  const int32_t* out_idx;  // output row of each token, or null (row = token)
+  int64_t out_rows;        // rows of out addressable through out_idx
   float* final_state;
   unsigned char* work;  // chunk records
   float lb_log2e;
@@ -92,6 +104,7 @@ inline int64_t chunk_slots(int N, int T_total) { return static_cast<int64_t>(T_t
 
 // Launchers (enqueue only; return the hipGetLastError() of the launch).
 hipError_t launch_verify(const VerifyParams& p, hipStream_t s);
+hipError_t launch_commit(const CommitParams& p, hipStream_t s);
 // Prefill phases: bit 0 = intra-chunk kernel, bit 1 = state-scan kernel.
 constexpr int PHASE_INTRA = 1;
 constexpr int PHASE_SCAN = 2;

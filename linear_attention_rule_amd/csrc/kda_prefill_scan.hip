@@ -154,11 +154,25 @@ struct ChunkCopy {
   uint32_t vrow_lane;
 };
 
+// The scatter indices of chunk jj's tokens (one per lane, rows past the chunk end
+// re-reading the last, in bounds) into the 64-entry LDS array at `lds`.  The copy
+// waves read them from there: a vector load the compiler tracks would make it wait
+// for the in-flight record copies it cannot see.
+__device__ __forceinline__ void copy_out_index(const PrefillParams& p, int cs, int ce, int jj,
+                                               int lane, uint32_t lds) {
+  const int tbj = cs + jj * CHUNK;
+  const int Lc = min(CHUNK, ce - tbj);
+  lds_dma4(uniform_addr(p.out_idx + tbj), static_cast<uint32_t>(min(lane, Lc - 1) * 4), lds);
+}
+
 // Stores the output tile of compute wave w for chunk jj (rows < chunk length) from LDS
-// to out: 16 bytes per lane, LANES_PER_ROW lanes per row.
+// to out: 16 bytes per lane, LANES_PER_ROW lanes per row.  With a scatter index (sidx:
+// the chunk's indices in LDS), token t goes to row out_idx[t] when that lies in
+// [0, out_rows).
 template <int NB>
-__device__ __forceinline__ void store_out_tile(const PrefillParams& p, const uint16_t* so, int cs,
-                                               int ce, int jj, int h, int v0, int lane) {
+__device__ __forceinline__ void store_out_tile(const PrefillParams& p, const uint16_t* so,
+                                               const int* sidx, int cs, int ce, int jj, int h,
+                                               int v0, int lane) {
   using VTl = VTile<NB>;
   const int tbj = cs + jj * CHUNK;
   const int Lc = min(CHUNK, ce - tbj);
@@ -167,9 +181,9 @@ __device__ __forceinline__ void store_out_tile(const PrefillParams& p, const uin
     const int row = lane / VTl::LANES_PER_ROW + VTl::ROWS_PER_COPY * i;
     const int col = 8 * (lane % VTl::LANES_PER_ROW);
     const uint4 val = *reinterpret_cast<const uint4*>(so + row * VTl::COLS + col);
-    if (row < Lc)
-      *reinterpret_cast<uint4*>(p.out + static_cast<int64_t>(tbj + row) * p.o_st + h * D + v0 +
-                                col) = val;
+    const int64_t orow = p.out_idx ? static_cast<int64_t>(sidx[row]) : tbj + row;
+    if (row < Lc && orow >= 0 && orow < p.out_rows)
+      *reinterpret_cast<uint4*>(p.out + orow * p.o_st + h * D + v0 + col) = val;
   }
 }
 
@@ -306,6 +320,7 @@ void prefill_scan_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char srec1[BUF_BYTES];
   __shared__ __attribute__((aligned(16))) uint32_t touch_sink[NC][64];
   __shared__ __attribute__((aligned(16))) uint16_t sout[2][NW][64 * VTl::COLS];
+  __shared__ __attribute__((aligned(16))) int sidx[2][64];   // scatter indices of a chunk
   constexpr int BV = 16 * NB * NW;
   constexpr int NVS = D / BV;
   const int tid = threadIdx.x;
@@ -354,8 +369,11 @@ void prefill_scan_kernel(PrefillParams p) {
       asm volatile("" ::: "memory");
       if (j + 1 < nch)
         CC(p, recbase, cs, ce, j + 1, h, v0, cw, has_vt, lane, (j & 1) ? lds0 : lds1, vt_off).all();
+      // Chunk j's scatter indices, read when its outputs are stored at the next chunk.
+      if (p.out_idx && cw == 0) copy_out_index(p, cs, ce, j, lane, lds_addr(sidx[j & 1]));
       if (j > 0 && has_vt)
-        store_out_tile<NB>(p, sout[(j - 1) & 1][w], cs, ce, j - 1, h, v0, lane);
+        store_out_tile<NB>(p, sout[(j - 1) & 1][w], sidx[(j - 1) & 1], cs, ce, j - 1, h, v0,
+                           lane);
       if (j + 1 < nch) {
         CC(p, recbase, cs, ce, min(j + 2, nch - 1), h, v0, cw, has_vt, lane, lds0, vt_off).touch(lane, sink);
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CC::NTOUCH) : "memory");
@@ -364,7 +382,8 @@ void prefill_scan_kernel(PrefillParams p) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (nch > 0 && has_vt)
-      store_out_tile<NB>(p, sout[(nch - 1) & 1][w], cs, ce, nch - 1, h, v0, lane);
+      store_out_tile<NB>(p, sout[(nch - 1) & 1][w], sidx[(nch - 1) & 1], cs, ce, nch - 1, h, v0,
+                         lane);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     return;
   }
@@ -425,6 +444,10 @@ void prefill_scan_kernel(PrefillParams p) {
         for (int r = 0; r < 4; ++r) dst[(16 * cb + 4 * g + r) * D] = S[nb][cb][r];
     }
   }
+  // Drain the final-state stores where the compiler sees it: its wait analysis joins
+  // this path with the copy waves' code, and stores it thinks pending there would make
+  // it wait inside the copy loop, on record copies it cannot see.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt unchanged
 }
 
 template <int NW, int NC, int NB>

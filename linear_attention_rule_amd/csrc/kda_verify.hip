@@ -45,6 +45,7 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p) {
   float* s_beta = s_v + T * BV;       // [T]
   float* s_kq = s_beta + T;           // [T]
   float* s_part = s_kq + T;           // [2 parity][4 waves][2 (r, y)][BV]
+  int* s_orow = reinterpret_cast<int*>(s_part + 2 * 4 * 2 * BV);   // [T] output rows
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -61,7 +62,9 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p) {
     // Padding row: zero outputs, no state rows written.
     for (int e = tid; e < T * BV; e += 256) {
       const int t = e / BV, c = e % BV;
-      p.out[static_cast<int64_t>(b * T + t) * p.o_st + h * D + v0 + c] = 0;
+      int64_t orow = static_cast<int64_t>(b) * T + t;
+      if (p.out_idx) orow = p.out_idx[orow];
+      if (orow >= 0 && orow < p.out_rows) p.out[orow * p.o_st + h * D + v0 + c] = 0;
     }
     return;
   }
@@ -97,6 +100,12 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p) {
       s_beta[t] = sigmoid_f32(bf16_to_f32(p.beta[tok * p.b_st + h]));
       s_kq[t] = sqk * rq * rk;
     }
+  }
+
+  // Output row of each step (the scatter index, when given).
+  for (int t = tid; t < T; t += 256) {
+    const int bt = b * T + t;
+    s_orow[t] = p.out_idx ? p.out_idx[bt] : bt;
   }
 
   // ---------------- gather the start state from the pool.
@@ -167,15 +176,17 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p) {
       const float s = p.scale;
       const uint32_t w0 = pack_bf16x2(s * (yy.x + kq * u.x), s * (yy.y + kq * u.y));
       const uint32_t w1 = pack_bf16x2(s * (yy.z + kq * u.z), s * (yy.w + kq * u.w));
-      uint16_t* o = p.out + (static_cast<int64_t>(b) * T + t) * p.o_st + h * D + v0 + 4 * cl;
-      *reinterpret_cast<uint2*>(o) = make_uint2(w0, w1);
+      const int64_t orow = s_orow[t];
+      if (orow >= 0 && orow < p.out_rows)
+        *reinterpret_cast<uint2*>(p.out + orow * p.o_st + h * D + v0 + 4 * cl) =
+            make_uint2(w0, w1);
     }
   }
 }
 
 template <int BV>
 size_t verify_lds_bytes(int T) {
-  return sizeof(float) * (static_cast<size_t>(T) * (3 * D + BV) + 2 * T + 2 * 4 * 2 * BV);
+  return sizeof(float) * (static_cast<size_t>(T) * (3 * D + BV) + 3 * T + 2 * 4 * 2 * BV);
 }
 
 template <int BV>

@@ -67,6 +67,23 @@ PREFILL_CASES = {c.name: c for c in (TINY, VARLEN, LONG, SINGLE_LONG)}
 VERIFY_CASES = {c.name: c for c in (VERIFY, VERIFY_B1)}
 
 
+@dataclass
+class MixedCase:
+    """One serving step carrying a prefill segment and speculative rows (MTP k draft
+    tokens per row: steps = k + 1), merged into one layer output of R rows."""
+    name: str
+    prefill: PrefillCase
+    spec: VerifyCase
+    extra_rows: int = 0            # rows of the layer output no token names
+    seed: int = 1006
+
+
+# Prefill segment 8 x 2048 with 64 spec rows of MTP k = 1 (2 tokens each), 16 heads.
+MIXED = MixedCase("mixed_8x2048_spec64x2_h16",
+                  PrefillCase("mixed_prefill_8x2048_h16", [2048] * 8, 16, init=None, seed=1007),
+                  VerifyCase("mixed_spec_64x2_h16_pool256", 64, 2, 16, 256, seed=1008))
+
+
 def _bf16(rng, shape, std=1.0):
     x = rng.standard_normal(size=shape, dtype=np.float32)
     if std != 1.0:
@@ -132,6 +149,24 @@ def make_verify(case: VerifyCase):
     return dict(q=q, k=k, v=v, g=g, beta_logits=beta_logits, A_log=A_log, dt_bias=dt_bias,
                 state_pool=pool, state_idx=torch.from_numpy(idx), num_steps=T,
                 lower_bound=case.lower_bound, scale=1.0 / math.sqrt(D))
+
+
+def make_mixed(case: MixedCase):
+    """Draw one mixed step: the prefill and spec workloads, the token order of the merged
+    layer output (non_spec_idx [T_prefill], spec_idx [B*T], int32, disjoint), the output
+    row count, and the accepted-token counts num_accepted [B] in 1..T."""
+    pre = make_prefill(case.prefill)
+    spec = make_verify(case.spec)
+    rng = np.random.default_rng(case.seed)
+    Tp = int(pre["q"].shape[0])
+    Ts = int(spec["q"].shape[0])
+    rows = Tp + Ts + case.extra_rows
+    order = rng.permutation(rows)[:Tp + Ts].astype(np.int32)
+    nacc = rng.integers(1, case.spec.steps + 1, size=case.spec.batch).astype(np.int32)
+    return dict(prefill=pre, spec=spec, out_rows=rows,
+                non_spec_idx=torch.from_numpy(order[:Tp].copy()),
+                spec_idx=torch.from_numpy(order[Tp:].copy()),
+                num_accepted=torch.from_numpy(nacc))
 
 
 def to_f64(t):

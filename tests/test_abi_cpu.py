@@ -23,13 +23,14 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = L.header_entry_points()
     assert set(names) >= {"kda_chunk_prefill", "kda_recurrent_verify", "kda_last_error",
-                          "kda_abi_version", "kda_chunk_prefill_workspace_size"}
+                          "kda_abi_version", "kda_chunk_prefill_workspace_size",
+                          "kda_commit_accepted"}
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_abi_version_and_workspace_size(lib):
-    assert lib.kda_abi_version() == 1
+    assert lib.kda_abi_version() == 2 == B.ABI_VERSION
     rec = 61 * 1024
     # chunk slots = floor(T/64) + N
     assert lib.kda_chunk_prefill_workspace_size(4, 32768, 16, 128) == (512 + 4) * 16 * rec
@@ -109,3 +110,45 @@ def test_zero_sized_calls_are_ok_without_launch(lib):
     assert _prefill(lib, _pdesc(N=0, T=0), ws_bytes=0) == KDA_OK
     assert _verify(lib, _vdesc(Bn=0)) == KDA_OK
     assert lib.kda_last_error() == b""
+
+
+def test_scatter_index_validation(lib):
+    # out_rows < 0 with an index
+    d = _pdesc(T=64, H=2)
+    d.out_token_index = 0x120000
+    d.out_rows = -1
+    assert _prefill(lib, d) == INVALID and b"out_rows" in lib.kda_last_error()
+    # misaligned index
+    d.out_rows = 10
+    d.out_token_index = 0x120002
+    assert _prefill(lib, d) == INVALID and b"aligned" in lib.kda_last_error()
+    # the index inside the output rows (out = fake(9), 10 rows of 256 bf16)
+    d.out_token_index = 0x90000 + 64
+    assert _prefill(lib, d) == INVALID and b"out_token_index" in lib.kda_last_error()
+    v = _vdesc()
+    v.out_token_index = 0x320000 + 16   # out = fake(50)
+    v.out_rows = 4
+    assert _verify(lib, v) == INVALID and b"out_token_index" in lib.kda_last_error()
+
+
+def _cdesc(Bn=2, T=8, H=2, D=128, slots=4):
+    return B.CommitDesc(Bn, T, H, D, slots)
+
+
+def _commit(lib, desc, inter=None, pool=None, null_idx=False):
+    f = _fake
+    return lib.kda_commit_accepted(inter if inter is not None else f(40), None if null_idx else f(7),
+                                   f(8), pool if pool is not None else f(20), ctypes.byref(desc),
+                                   None)
+
+
+def test_commit_rejects_bad_arguments(lib):
+    assert _commit(lib, _cdesc(D=64)) == UNSUPPORTED
+    assert _commit(lib, _cdesc(T=0)) == INVALID
+    assert _commit(lib, _cdesc(slots=0)) == INVALID
+    assert _commit(lib, _cdesc(H=0)) == INVALID
+    assert _commit(lib, _cdesc(), null_idx=True) == INVALID
+    assert _commit(lib, _cdesc(), inter=_fake(20)) == INVALID
+    assert b"overlap" in lib.kda_last_error()
+    assert lib.kda_commit_accepted(_fake(40), _fake(7), _fake(8), _fake(20), None, None) == INVALID
+    assert _commit(lib, _cdesc(Bn=0)) == KDA_OK
