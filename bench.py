@@ -25,6 +25,7 @@ import argparse
 import json
 import math
 import os
+import re
 import resource
 import sys
 import time
@@ -90,6 +91,7 @@ KERNEL_SOURCES = {
                          "linear_attention_rule_amd/csrc/kda_prefill_common.h"),
     "kda_verify": ("linear_attention_rule_amd/csrc/kda_verify.hip",),
     "kda_commit": ("linear_attention_rule_amd/csrc/kda_commit.hip",),
+    "kda_seg_combine": ("linear_attention_rule_amd/csrc/kda_prefill_scan.hip",),
 }
 # rocprofv3 kernel names -> the names used in this benchmark.
 KERNEL_PATTERNS = {
@@ -97,6 +99,7 @@ KERNEL_PATTERNS = {
     "kda_prefill_scan": "prefill_scan_kernel",
     "kda_verify": "verify_kernel",
     "kda_commit": "commit_kernel",
+    "kda_seg_combine": "seg_combine_kernel",
 }
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 CALIB_BYTES = 1 << 30
@@ -125,7 +128,14 @@ def stored_traffic(kernel, workload):
 
 
 MAIN_WORKLOAD = f"prefill {W.LONG.name} + verify {W.VERIFY.name}"
-EXTRAS_WORKLOAD = f"commit after {W.VERIFY.name} + mixed step {W.MIXED.name}"
+EXTRAS_WORKLOAD = (f"commit after {W.VERIFY.name} + segmented prefill {W.SINGLE_LONG.name} "
+                   f"+ mixed step {W.MIXED.name}")
+
+
+def targs(kernel_name):
+    """Template arguments of a (demangled) kernel name, e.g. '<4, 4, 1, 1>' (or '')."""
+    m = re.search(r"_kernel(<[^()]*>)\(", kernel_name)
+    return m.group(1) if m else ""
 
 
 def summarize(prof_dirs, workload, out_md, mode_flag):
@@ -145,7 +155,8 @@ def summarize(prof_dirs, workload, out_md, mode_flag):
                 for k, pat in KERNEL_PATTERNS.items():
                     if pat in r["Kernel_Name"]:
                         dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
-                        stats.setdefault(k, []).append(dur)
+                        stats.setdefault((k, targs(r["Kernel_Name"]), int(r["Grid_Size_X"])),
+                                         []).append(dur)
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             for r in csv.DictReader(open(f)):
                 name, cname, val = r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])
@@ -154,7 +165,8 @@ def summarize(prof_dirs, workload, out_md, mode_flag):
                     calib.setdefault(cname, []).append(val)
                 for k, pat in KERNEL_PATTERNS.items():
                     if pat in name:
-                        counters.setdefault(k, {}).setdefault(cname, []).append(val)
+                        counters.setdefault((k, targs(name), int(r["Grid_Size"])),
+                                            {}).setdefault(cname, []).append(val)
     factors = {}
     for cname in ("FETCH_SIZE", "WRITE_SIZE"):
         big = [v for v in calib.get(cname, []) if v * 1024 > 0.5 * CALIB_BYTES]
@@ -173,8 +185,17 @@ def summarize(prof_dirs, workload, out_md, mode_flag):
              f"{mode_flag} --summary-out <this file>", "",
              "Kernel durations (kernel-trace run only):", "",
              "| kernel | dispatches | avg us | min us | max us |", "|---|---|---|---|---|"]
-    for k, v in sorted(stats.items()):
-        lines.append(f"| {k} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+    def label(key, keys):
+        # A kernel launched in one form keeps its plain name; else its template arguments
+        # and grid size tell apart the launches it made.
+        k, ta, grid = key
+        if sum(1 for kk, _, _ in keys if kk == k) == 1:
+            return k
+        return f"{k} [{ta + ', ' if ta else ''}grid {grid}]"
+
+    for key, v in sorted(stats.items()):
+        lines.append(f"| {label(key, stats)} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | "
+                     f"{max(v):.2f} |")
     lines += ["", "Counter calibration (--calib-copy: an elementwise kernel reading and writing "
               "1 GiB): bytes = counter KiB x 1024 x factor, with "
               + ", ".join(f"{c} factor {f:.4f}" if f else f"{c}: not measured"
@@ -186,7 +207,8 @@ def summarize(prof_dirs, workload, out_md, mode_flag):
         store = {}
     lines += ["| kernel | FETCH_SIZE KiB/dispatch (raw) | WRITE_SIZE KiB/dispatch (raw) | "
               "calibrated HBM MB/dispatch |", "|---|---|---|---|"]
-    for k, cs in sorted(counters.items()):
+    for key, cs in sorted(counters.items()):
+        k = label(key, counters)
         fr = cs.get("FETCH_SIZE")
         wr = cs.get("WRITE_SIZE")
         if not fr or not wr:
@@ -197,7 +219,7 @@ def summarize(prof_dirs, workload, out_md, mode_flag):
         lines.append(f"| {k} | {f_kib:.1f} | {w_kib:.1f} | {(fb + wb) / 1e6:.1f} |")
         if factors["FETCH_SIZE"] and factors["WRITE_SIZE"]:
             store[f"{k}@{workload}"] = {"fetch_bytes": fb, "write_bytes": wb,
-                                       "source_hash": source_hash(k),
+                                       "source_hash": source_hash(key[0]),
                                        "calibration": factors}
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -276,6 +298,27 @@ def bench_next_rows(iters):
                          out_token_index=sp_idx)
 
     t_mixed = time_calls(mixed, iters)
+    del core, ws, fin, sinter
+
+    # One long sequence with a gathered start state: few (sequence, head) pairs, so the
+    # scan runs segment-parallel (state maps per segment, combine, then the segments).
+    sc = W.SINGLE_LONG
+    sd = to_dev(W.make_prefill(sc))
+    Ts1, Hs1 = sd["q"].shape[0], sd["q"].shape[1]
+    s_ws = torch.empty(prefill_workspace_bytes(1, Ts1, Hs1), dtype=torch.uint8, device="cuda")
+    s_out = torch.empty((Ts1, Hs1, D), dtype=torch.bfloat16, device="cuda")
+    s_fin = torch.empty((1, Hs1, D, D), dtype=torch.float32, device="cuda")
+
+    def single(phase):
+        chunk_prefill(sd["q"], sd["k"], sd["v"], sd["g"], sd["beta_logits"], sd["A_log"],
+                      sd["dt_bias"], sd["lower_bound"], sd["cu_seqlens"],
+                      initial_state=sd["initial_state"], initial_state_idx=sd["initial_state_idx"],
+                      out=s_out, final_state=s_fin, workspace=s_ws, scale=sd["scale"], phase=phase)
+
+    t_s_intra = time_calls(lambda: single("intra"), iters)
+    t_s_scan = time_calls(lambda: single("scan"), iters)
+    s_bytes = Ts1 * Hs1 * BYTES_PER_TOKEN_HEAD + 2 * Hs1 * STATE_BYTES
+    t_single = t_s_intra + t_s_scan
     tokens = Tp + Bs * Ts
     mixed_bytes = (tokens * Hm * BYTES_PER_TOKEN_HEAD + Np * Hm * STATE_BYTES
                    + Bs * Hm * STATE_BYTES * (1 + Ts))
@@ -284,6 +327,12 @@ def bench_next_rows(iters):
     return {
         "commit": {"workload": f"commit after {vcase.name}", "us": round(t_commit * 1e6, 2),
                    "roofline": rl_commit, "algorithmic_bytes": commit_bytes},
+        "segmented_prefill": {"workload": sc.name, "us": round(t_single * 1e6, 2),
+                              "intra_us": round(t_s_intra * 1e6, 2),
+                              "scan_us": round(t_s_scan * 1e6, 2),
+                              "tokens_per_s": round(Ts1 / t_single, 1),
+                              "roofline": roofline(s_bytes, 0, t_single),
+                              "algorithmic_bytes": s_bytes},
         "mixed_step": {"workload": W.MIXED.name, "us": round(t_mixed * 1e6, 2),
                        "tokens_per_s": round(tokens / t_mixed, 1),
                        "roofline": roofline(mixed_bytes, 0, t_mixed),

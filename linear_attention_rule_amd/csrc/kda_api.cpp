@@ -95,8 +95,9 @@ const char* kda_last_error(void) { return g_last_error.c_str(); }
 size_t kda_chunk_prefill_workspace_size(int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
                                         int32_t head_dim) {
   if (num_seqs < 0 || total_tokens < 0 || num_heads < 1 || head_dim != KDA_HEAD_DIM) return 0;
-  return static_cast<size_t>(kda::chunk_slots(num_seqs, total_tokens)) *
-         static_cast<size_t>(num_heads) * static_cast<size_t>(kda::REC_BYTES);
+  const int64_t rec = kda::prefill_record_bytes(num_seqs, total_tokens, num_heads);
+  if (rec == 0) return 0;
+  return static_cast<size_t>(rec + kda::prefill_segment_bytes(num_seqs, num_heads));
 }
 
 }  // extern "C"
@@ -180,6 +181,10 @@ kda_status prefill_phases(const void* q, const void* k, const void* v, const voi
   p.out_rows = orows;
   p.final_state = final_state;
   p.work = static_cast<unsigned char*>(workspace);
+  p.seg_ws = kda::prefill_segment_bytes(N, H) > 0 && kda::prefill_record_bytes(N, T, H) > 0
+                 ? reinterpret_cast<float*>(p.work + kda::prefill_record_bytes(N, T, H))
+                 : nullptr;
+  p.seg_G = 1;
   p.lb_log2e = lower_bound * kda::LOG2E;
   p.scale = desc->scale > 0.f ? desc->scale : 1.0f / std::sqrt(static_cast<float>(KDA_HEAD_DIM));
   p.N = N;

@@ -82,6 +82,8 @@ struct PrefillParams {
   const int32_t* out_idx;  // output row of each token, or null (row = token)
   int64_t out_rows;        // rows of out addressable through out_idx
   float* final_state;
+  float* seg_ws;           // segment-parallel scan states, or null (not available)
+  int seg_G;               // segments per sequence (set by launch_prefill; 1 = none)
   unsigned char* work;  // chunk records
   float lb_log2e;
   float scale;
@@ -111,5 +113,22 @@ constexpr int PHASE_SCAN = 2;
 hipError_t launch_prefill(const PrefillParams& p, int phases, hipStream_t s);
 // The intra-chunk kernel alone (called by launch_prefill).
 hipError_t launch_prefill_intra(const PrefillParams& p, hipStream_t s);
+
+// Segment-parallel scan: at most SEG_MAX segments per sequence, used only when
+// N * H <= SEG_MAX_PAIRS (the workspace holds SEG_SLOTS states per pair then).
+constexpr int SEG_MAX = 8;
+constexpr int SEG_SLOTS = 3 * SEG_MAX - 5;
+constexpr int SEG_MIN_CHUNKS = 4;
+constexpr int SEG_MAX_PAIRS = 32;
+// Segments the scan uses for these shapes on a device with `cus` CUs (1 = none).
+int prefill_segments(int N, int T_total, int H, int cus);
+// Workspace bytes: the chunk records, then (when N * H <= SEG_MAX_PAIRS) the segment states.
+inline int64_t prefill_record_bytes(int N, int T_total, int H) {
+  return chunk_slots(N, T_total) * H * REC_BYTES;
+}
+inline int64_t prefill_segment_bytes(int N, int H) {
+  const int64_t pairs = static_cast<int64_t>(N) * H;
+  return pairs <= SEG_MAX_PAIRS ? pairs * SEG_SLOTS * D * D * 4 : 0;
+}
 
 }  // namespace kda

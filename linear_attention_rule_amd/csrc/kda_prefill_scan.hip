@@ -12,6 +12,8 @@
 //   global_load_lds_dwordx4, pull the chunk after next into L2, and store the
 //   output tiles the compute waves leave in LDS, so the compute waves run only
 //   LDS reads and MFMAs while the next chunk is in flight.
+#include <algorithm>
+
 #include "kda_prefill_common.h"
 
 namespace kda {
@@ -194,8 +196,8 @@ __device__ __forceinline__ void store_out_tile(const PrefillParams& p, const uin
 template <int NB>
 __device__ __forceinline__ void scan_chunk(const unsigned char* __restrict__ R,
                                            const unsigned char* __restrict__ VT,
-                                           uint16_t* __restrict__ SO, int Lc, int lane,
-                                           f32x4 (&S)[NB][8]) {
+                                           uint16_t* __restrict__ SO, int Lc, bool zero_v,
+                                           bool write_out, int lane, f32x4 (&S)[NB][8]) {
   const int nl = lane & 15, g = lane >> 4;
   const uint16_t* vt = reinterpret_cast<const uint16_t*>(VT);
   half8 Sf[NB][4];
@@ -214,7 +216,7 @@ __device__ __forceinline__ void scan_chunk(const unsigned char* __restrict__ R,
       for (int r = 0; r < 4; ++r) {
         const int tt = 16 * tb + 4 * g + r;
         const float vv = bf16_to_f32(vt[tt * (16 * NB) + 16 * nb + nl]);
-        X[nb][tb][r] = (tt < Lc) ? vv : 0.f;
+        X[nb][tb][r] = (tt < Lc && !zero_v) ? vv : 0.f;
       }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -255,33 +257,35 @@ __device__ __forceinline__ void scan_chunk(const unsigned char* __restrict__ R,
   }
 
   // O^T = S^T (scale Q_Gamma)^T + U^T (scale tril P)^T; lane (token, g) holds 4 value columns.
+  if (write_out) {
 #pragma unroll
-  for (int tb = 0; tb < 4; ++tb) {
-    f32x4 o[NB];
+    for (int tb = 0; tb < 4; ++tb) {
+      f32x4 o[NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const half8 bq = frag(R, FR_QG + 4 * tb + s, lane);
+      for (int s = 0; s < 4; ++s) {
+        const half8 bq = frag(R, FR_QG + 4 * tb + s, lane);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) o[nb] = mfma_f16(Sf[nb][s], bq, o[nb]);
+        for (int nb = 0; nb < NB; ++nb) o[nb] = mfma_f16(Sf[nb][s], bq, o[nb]);
+      }
+      const int fi = (tb < 2) ? tb : 2 + 2 * (tb - 2);
+      {
+        const half8 bp = frag(R, FR_PM + fi, lane);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) o[nb] = mfma_f16(Uf[nb][0], bp, o[nb]);
+      }
+      if (tb >= 2) {
+        const half8 bp = frag(R, FR_PM + fi + 1, lane);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) o[nb] = mfma_f16(Uf[nb][1], bp, o[nb]);
+      }
+      uint16_t* orow = SO + (16 * tb + nl) * (16 * NB) + 4 * g;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        *reinterpret_cast<uint2*>(orow + 16 * nb) =
+            make_uint2(pack_bf16x2(o[nb][0], o[nb][1]), pack_bf16x2(o[nb][2], o[nb][3]));
     }
-    const int fi = (tb < 2) ? tb : 2 + 2 * (tb - 2);
-    {
-      const half8 bp = frag(R, FR_PM + fi, lane);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) o[nb] = mfma_f16(Uf[nb][0], bp, o[nb]);
-    }
-    if (tb >= 2) {
-      const half8 bp = frag(R, FR_PM + fi + 1, lane);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) o[nb] = mfma_f16(Uf[nb][1], bp, o[nb]);
-    }
-    uint16_t* orow = SO + (16 * tb + nl) * (16 * NB) + 4 * g;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      *reinterpret_cast<uint2*>(orow + 16 * nb) =
-          make_uint2(pack_bf16x2(o[nb][0], o[nb][1]), pack_bf16x2(o[nb][2], o[nb][3]));
   }
   // S <- Diag(Gamma_C) S + K_C^T U
   const float* gam = reinterpret_cast<const float*>(R + REC_GAMMA_OFF);
@@ -301,16 +305,123 @@ __device__ __forceinline__ void scan_chunk(const unsigned char* __restrict__ R,
   }
 }
 
+// What one scan workgroup does: a chunk range of one (sequence, head) pair for one
+// slice of value columns, from a start state, optionally writing outputs and a final
+// state.
+constexpr int START_INIT = 0;    // the caller's initial state (direct, gathered, or zero)
+constexpr int START_ZERO = 1;
+constexpr int START_IDENT = 2;   // identity columns: the segment's state map
+constexpr int START_WS = 3;      // a state in the segment workspace
+
+struct ScanWork {
+  int n, h, vs, jb, je;          // sequence, head, value slice, chunks [jb, je)
+  int start;
+  const float* start_blk;        // START_WS: the [128][128] start state
+  float* fin_blk;                // [128][128] destination of the end state, or null
+  bool zero_v, write_out;
+};
+
+// Workspace of the segment-parallel scan: per (sequence, head), SEG_SLOTS states of
+// [128][128] fp32.  Slot s-1 holds the start state S_in(s) of segment s (1 <= s < G);
+// slot (G-1) + (s-1) the map M_s and slot 2(G-1) - 1 + (s-1) the offset B_s of middle
+// segment s (1 <= s <= G-2), where S_out(s) = M_s S_in(s) + B_s.
+__device__ __forceinline__ float* seg_slot(const PrefillParams& p, int n, int h, int slot) {
+  return p.seg_ws + ((static_cast<int64_t>(n) * p.H + h) * SEG_SLOTS + slot) * (D * D);
+}
+__device__ __forceinline__ int seg_m_slot(int G, int s) { return (G - 1) + (s - 1); }
+__device__ __forceinline__ int seg_b_slot(int G, int s) { return (G - 1) + (G - 2) + (s - 1); }
+
+// Chunks [jb, je) of segment s of G over a sequence of nch chunks.
+__device__ __forceinline__ int seg_begin(int nch, int G, int s) {
+  return static_cast<int>(static_cast<int64_t>(nch) * s / G);
+}
+
+// MODE_SEQ: whole sequences.  MODE_SEG_A: segment 0 with outputs, and the state maps
+// (M_s, B_s) of the middle segments.  MODE_SEG_C: segments 1..G-1 from their start
+// states, with outputs.
+constexpr int MODE_SEQ = 0;
+constexpr int MODE_SEG_A = 1;
+constexpr int MODE_SEG_C = 2;
+
+// Workgroups per unit of work (a pair, or a pair's segment) and the workgroup -> unit
+// order: ids are dealt round-robin to the 8 XCDs (id % 8), so the workgroups of one
+// unit get ids congruent mod 8 and share one L2 for the records they all read.
+template <int MODE, int NVS>
+__device__ __forceinline__ bool decode_work(const PrefillParams& p, ScanWork& wk) {
+  constexpr int PER_UNIT = (MODE == MODE_SEG_A) ? 2 * NVS : NVS;
+  const int H = p.H;
+  const int pairs = p.N * H;
+  const int G = p.seg_G;
+  const int units = (MODE == MODE_SEQ) ? pairs : pairs * (G - 1);
+  const int blk = blockIdx.x;
+  const int grp = blk / (8 * PER_UNIT), rr = blk % (8 * PER_UNIT);
+  const int cg = rr / 8;
+  const int unit = grp * 8 + (rr & 7);
+  if (unit >= units) return false;
+  const int pair = (MODE == MODE_SEQ) ? unit : unit / (G - 1);
+  wk.n = pair / H;
+  wk.h = pair % H;
+  const int len = p.cu[wk.n + 1] - p.cu[wk.n];
+  const int nch = (len + CHUNK - 1) / CHUNK;
+  wk.start_blk = nullptr;
+  wk.zero_v = false;
+  wk.write_out = true;
+  if (MODE == MODE_SEQ) {
+    wk.vs = cg;
+    wk.jb = 0;
+    wk.je = nch;
+    wk.start = START_INIT;
+    wk.fin_blk = p.final_state ? p.final_state + (static_cast<int64_t>(wk.n) * H + wk.h) * (D * D)
+                               : nullptr;
+    return true;
+  }
+  if (MODE == MODE_SEG_A) {
+    const int s = unit % (G - 1);        // segments 0 .. G-2
+    wk.jb = seg_begin(nch, G, s);
+    wk.je = seg_begin(nch, G, s + 1);
+    if (s == 0) {
+      if (cg >= NVS) return false;
+      wk.vs = cg;
+      wk.start = START_INIT;
+      wk.fin_blk = seg_slot(p, wk.n, wk.h, 0);          // S_in(1)
+      return true;
+    }
+    wk.write_out = false;
+    if (cg < NVS) {                      // the map M_s: identity columns, no values
+      wk.vs = cg;
+      wk.start = START_IDENT;
+      wk.zero_v = true;
+      wk.fin_blk = seg_slot(p, wk.n, wk.h, seg_m_slot(G, s));
+    } else {                             // the offset B_s: zero start, the values
+      wk.vs = cg - NVS;
+      wk.start = START_ZERO;
+      wk.fin_blk = seg_slot(p, wk.n, wk.h, seg_b_slot(G, s));
+    }
+    return true;
+  }
+  const int s = 1 + unit % (G - 1);      // MODE_SEG_C: segments 1 .. G-1
+  wk.vs = cg;
+  wk.jb = seg_begin(nch, G, s);
+  wk.je = seg_begin(nch, G, s + 1);
+  wk.start = START_WS;
+  wk.start_blk = seg_slot(p, wk.n, wk.h, s - 1);
+  wk.fin_blk = (s == G - 1 && p.final_state)
+                   ? p.final_state + (static_cast<int64_t>(wk.n) * H + wk.h) * (D * D)
+                   : nullptr;
+  return true;
+}
+
 // Workgroup: NW compute waves (wave w owns value columns v0 .. v0 + 16 NB) and NC >= NW
-// copy waves (copy wave c < NW serves compute wave c's value and output tiles).  A wave that issues a whole chunk's copies stalls at issue until the copy
-// engine has drained most of them, and copies issued piecemeal during the compute land
-// too late; so all vector-memory work goes to waves of their own: they issue a chunk's
-// copies at once at the start of the previous chunk and wait for them, and store the
-// output tiles the compute waves leave in LDS.  The compute waves only read LDS and
-// run MFMAs.  One barrier per chunk plus a final one: when every wave has reached
-// barrier j, chunk j has landed in buffer j%2, chunk j-1's buffer is free and chunk
+// copy waves (copy wave c < NW serves compute wave c's value and output tiles).  A wave
+// that issues a whole chunk's copies stalls at issue until the copy engine has drained
+// most of them, and copies issued piecemeal during the compute land too late; so all
+// vector-memory work goes to waves of their own: they issue a chunk's copies at once at
+// the start of the previous chunk and wait for them, and store the output tiles the
+// compute waves leave in LDS.  The compute waves only read LDS and run MFMAs.  One
+// barrier per chunk plus a final one: when every wave has reached the barrier of chunk
+// j, chunk j has landed in buffer (j - jb) % 2, chunk j-1's buffer is free and chunk
 // j-1's output tiles are complete.
-template <int NW, int NC, int NB>
+template <int NW, int NC, int NB, int MODE>
 __global__ __launch_bounds__(64 * (NW + NC))
 __attribute__((amdgpu_waves_per_eu((NW + NC + 3) / 4, (NW + NC + 3) / 4)))
 void prefill_scan_kernel(PrefillParams p) {
@@ -323,6 +434,8 @@ void prefill_scan_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) int sidx[2][64];   // scatter indices of a chunk
   constexpr int BV = 16 * NB * NW;
   constexpr int NVS = D / BV;
+  ScanWork wk;
+  if (!decode_work<MODE, NVS>(p, wk)) return;   // uniform: the whole workgroup exits
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool copier = wave >= NW;
@@ -330,24 +443,12 @@ void prefill_scan_kernel(PrefillParams p) {
   const bool has_vt = cw < NW;               // copy wave serves compute wave cw
   const int w = copier ? (has_vt ? cw : 0) : wave;   // compute wave served / owned
   const int lane = tid & 63, nl = lane & 15, g = lane >> 4;
-  // XCD-aware order: workgroup ids are dealt round-robin to the 8 XCDs (id % 8),
-  // so the NVS value slices of one (sequence, head) pair get ids congruent mod 8
-  // and share one L2 for the record they all read.
   const int H = p.H;
-  const int pairs = p.N * H;
-  const int blk = blockIdx.x;
-  const int grp = blk / (8 * NVS), rr = blk % (8 * NVS);
-  const int vs = rr / 8;
-  const int pair = grp * 8 + (rr & 7);
-  if (pair >= pairs) return;
-  const int n = pair / H;
-  const int h = pair % H;
-  const int v0 = vs * BV + 16 * NB * w;   // first value column of compute wave w
+  const int n = wk.n, h = wk.h, jb = wk.jb, je = wk.je;
+  const int v0 = wk.vs * BV + 16 * NB * w;   // first value column of compute wave w
   const int cs = p.cu[n], ce = p.cu[n + 1];
   const int len = ce - cs;
-  const int nch = (len + CHUNK - 1) / CHUNK;
   const int64_t slot0 = cs / CHUNK + n;
-  const int64_t HDD = static_cast<int64_t>(D) * D;
   const unsigned char* recbase = p.work + (slot0 * H + h) * REC_BYTES;
   const int vt_off = REC_BYTES + w * VTl::BYTES;
 
@@ -357,33 +458,39 @@ void prefill_scan_kernel(PrefillParams p) {
     // counts in issue order, so NTOUCH outstanding operations left means exactly the
     // touches are still in flight.
     using CC = ChunkCopy<NC, NB>;
+    const bool copy_vt = has_vt && !wk.zero_v;
+    const bool store = has_vt && wk.write_out;
     const uint32_t lds0 = lds_addr(srec0), lds1 = lds_addr(srec1);
     const uint32_t sink = lds_addr(touch_sink[cw]);
-    for (int j = 0; j < nch; ++j) {
-      if (j == 0) {
-        CC(p, recbase, cs, ce, 0, h, v0, cw, has_vt, lane, lds0, vt_off).all();
-        CC(p, recbase, cs, ce, min(1, nch - 1), h, v0, cw, has_vt, lane, lds1, vt_off).touch(lane, sink);
+    for (int j = jb; j < je; ++j) {
+      const int par = (j - jb) & 1;
+      if (j == jb) {
+        CC(p, recbase, cs, ce, jb, h, v0, cw, copy_vt, lane, lds0, vt_off).all();
+        CC(p, recbase, cs, ce, min(jb + 1, je - 1), h, v0, cw, copy_vt, lane, lds1, vt_off)
+            .touch(lane, sink);
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CC::NTOUCH) : "memory");
       }
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      if (j + 1 < nch)
-        CC(p, recbase, cs, ce, j + 1, h, v0, cw, has_vt, lane, (j & 1) ? lds0 : lds1, vt_off).all();
+      if (j + 1 < je)
+        CC(p, recbase, cs, ce, j + 1, h, v0, cw, copy_vt, lane, par ? lds0 : lds1, vt_off).all();
       // Chunk j's scatter indices, read when its outputs are stored at the next chunk.
-      if (p.out_idx && cw == 0) copy_out_index(p, cs, ce, j, lane, lds_addr(sidx[j & 1]));
-      if (j > 0 && has_vt)
-        store_out_tile<NB>(p, sout[(j - 1) & 1][w], sidx[(j - 1) & 1], cs, ce, j - 1, h, v0,
-                           lane);
-      if (j + 1 < nch) {
-        CC(p, recbase, cs, ce, min(j + 2, nch - 1), h, v0, cw, has_vt, lane, lds0, vt_off).touch(lane, sink);
+      if (wk.write_out && p.out_idx && cw == 0)
+        copy_out_index(p, cs, ce, j, lane, lds_addr(sidx[par]));
+      if (j > jb && store)
+        store_out_tile<NB>(p, sout[par ^ 1][w], sidx[par ^ 1], cs, ce, j - 1, h, v0, lane);
+      if (j + 1 < je) {
+        CC(p, recbase, cs, ce, min(j + 2, je - 1), h, v0, cw, copy_vt, lane, lds0, vt_off)
+            .touch(lane, sink);
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CC::NTOUCH) : "memory");
       }
     }
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (nch > 0 && has_vt)
-      store_out_tile<NB>(p, sout[(nch - 1) & 1][w], sidx[(nch - 1) & 1], cs, ce, nch - 1, h, v0,
-                         lane);
+    if (je > jb && store) {
+      const int par = (je - 1 - jb) & 1;
+      store_out_tile<NB>(p, sout[par][w], sidx[par], cs, ce, je - 1, h, v0, lane);
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     return;
   }
@@ -391,53 +498,60 @@ void prefill_scan_kernel(PrefillParams p) {
   // Start state: S[nb][cb][r] = S[16cb + 4g + r][v0 + 16nb + nl].
   f32x4 S[NB][8];
   {
-    int row = -1;
-    if (p.init) {
+    const float* src_blk = nullptr;
+    if (wk.start == START_INIT && p.init) {
+      int row = n;
       if (p.init_idx) {
         const int ri = p.init_idx[n];
         row = (ri >= 0 && ri < p.init_rows) ? ri : -1;
-      } else {
-        row = n;
       }
+      if (row >= 0) src_blk = p.init + (static_cast<int64_t>(row) * H + h) * (D * D);
+    } else if (wk.start == START_WS) {
+      src_blk = wk.start_blk;
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      if (row >= 0) {
-        const float* src = p.init + (static_cast<int64_t>(row) * H + h) * HDD + v0 + 16 * nb + nl;
+      const int col = v0 + 16 * nb + nl;
+      if (src_blk) {
+        const float* src = src_blk + col;
 #pragma unroll
         for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) S[nb][cb][r] = src[(16 * cb + 4 * g + r) * D];
       } else {
+        const float one = (wk.start == START_IDENT) ? 1.f : 0.f;
 #pragma unroll
-        for (int cb = 0; cb < 8; ++cb) S[nb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) S[nb][cb][r] = (16 * cb + 4 * g + r == col) ? one : 0.f;
       }
     }
   }
 
   // Two chunks per trip so each half reads one fixed LDS buffer.
-  for (int j = 0; j < nch; j += 2) {
+  for (int j = jb; j < je; j += 2) {
     // Reads of the buffer about to be refilled are complete once lgkmcnt is zero.
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    scan_chunk<NB>(srec0, srec0 + vt_off, sout[0][w], min(CHUNK, len - j * CHUNK), lane, S);
-    if (j + 1 >= nch) break;
+    scan_chunk<NB>(srec0, srec0 + vt_off, sout[0][w], min(CHUNK, len - j * CHUNK), wk.zero_v,
+                   wk.write_out, lane, S);
+    if (j + 1 >= je) break;
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    scan_chunk<NB>(srec1, srec1 + vt_off, sout[1][w], min(CHUNK, len - (j + 1) * CHUNK), lane,
-                   S);
+    scan_chunk<NB>(srec1, srec1 + vt_off, sout[1][w], min(CHUNK, len - (j + 1) * CHUNK),
+                   wk.zero_v, wk.write_out, lane, S);
   }
   // Output tiles of the last chunk complete before the copy waves store them.
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 
-  if (p.final_state) {
+  if (wk.fin_blk) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      float* dst = p.final_state + (static_cast<int64_t>(n) * H + h) * HDD + v0 + 16 * nb + nl;
+      float* dst = wk.fin_blk + v0 + 16 * nb + nl;
 #pragma unroll
       for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
@@ -450,36 +564,124 @@ void prefill_scan_kernel(PrefillParams p) {
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt unchanged
 }
 
-template <int NW, int NC, int NB>
+// Segment start states: S_in(1) comes from segment 0; then, for each middle segment s in
+// order, S_in(s+1) = M_s S_in(s) + B_s in fp32.  One workgroup per (sequence, head,
+// 32-column slice); thread t computes rows 4(t/8) .. +3 and columns 4(t%8) .. +3 of the
+// slice, reading rows of M_s from global memory and the slice of S_in(s) from LDS.
+constexpr int COMB_COLS = 32;
+__global__ __launch_bounds__(256) void seg_combine_kernel(PrefillParams p) {
+  __shared__ __attribute__((aligned(16))) float sin_s[D][COMB_COLS];
+  const int G = p.seg_G;
+  const int slices = D / COMB_COLS;
+  const int pair = blockIdx.x / slices;
+  const int c0 = (blockIdx.x % slices) * COMB_COLS;
+  const int n = pair / p.H, h = pair % p.H;
+  const int tid = threadIdx.x;
+  const int r0 = 4 * (tid >> 3);            // rows r0 .. r0 + 3
+  const int cq = 4 * (tid & 7);             // columns cq .. cq + 3 of the slice
+  for (int s = 1; s <= G - 2; ++s) {
+    const float* sin = seg_slot(p, n, h, s - 1);
+    const float* M = seg_slot(p, n, h, seg_m_slot(G, s));
+    const float* B = seg_slot(p, n, h, seg_b_slot(G, s));
+    float* sout = seg_slot(p, n, h, s);
+    __syncthreads();   // the previous step's reads of sin_s are done
+    for (int e = tid; e < D * COMB_COLS / 4; e += 256) {
+      const int r = e / (COMB_COLS / 4), c = 4 * (e % (COMB_COLS / 4));
+      *reinterpret_cast<float4*>(&sin_s[r][c]) =
+          *reinterpret_cast<const float4*>(sin + r * D + c0 + c);
+    }
+    __syncthreads();
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 b4 = *reinterpret_cast<const float4*>(B + (r0 + i) * D + c0 + cq);
+      acc[i][0] = b4.x; acc[i][1] = b4.y; acc[i][2] = b4.z; acc[i][3] = b4.w;
+    }
+    for (int k = 0; k < D; k += 4) {
+      float4 m4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m4[i] = *reinterpret_cast<const float4*>(M + (r0 + i) * D + k);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const float4 x = *reinterpret_cast<const float4*>(&sin_s[k + kk][cq]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float m = (kk == 0) ? m4[i].x : (kk == 1) ? m4[i].y : (kk == 2) ? m4[i].z : m4[i].w;
+          acc[i][0] += m * x.x;
+          acc[i][1] += m * x.y;
+          acc[i][2] += m * x.z;
+          acc[i][3] += m * x.w;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<float4*>(sout + (r0 + i) * D + c0 + cq) =
+          make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+    // The next step reads this slice of S_in(s+1) back after the barrier at its top.
+  }
+}
+
+template <int NW, int NC, int NB, int MODE>
 hipError_t launch_scan(const PrefillParams& p, hipStream_t s) {
+  constexpr int NVS = D / (16 * NB * NW);
+  constexpr int PER_UNIT = (MODE == MODE_SEG_A) ? 2 * NVS : NVS;
   const int64_t pairs = static_cast<int64_t>(p.N) * p.H;
-  const int64_t groups = (pairs + 7) / 8;
-  const dim3 grid(static_cast<unsigned>(groups * 8 * (D / (16 * NB * NW))));
-  hipLaunchKernelGGL((prefill_scan_kernel<NW, NC, NB>), grid, dim3(64 * (NW + NC)), 0, s, p);
+  const int64_t units = (MODE == MODE_SEQ) ? pairs : pairs * (p.seg_G - 1);
+  const int64_t groups = (units + 7) / 8;
+  const dim3 grid(static_cast<unsigned>(groups * 8 * PER_UNIT));
+  hipLaunchKernelGGL((prefill_scan_kernel<NW, NC, NB, MODE>), grid, dim3(64 * (NW + NC)), 0, s,
+                     p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillParams& p, int phases, hipStream_t s) {
-  if (p.N == 0) return hipSuccess;
+int prefill_segments(int N, int T_total, int H, int cus) {
+  // Segments pay off when the pairs leave most CUs idle and sequences are long: the
+  // critical path goes from G segment lengths to about two, for about three times the
+  // scan work spread over otherwise idle CUs.  G is the largest count whose phase A
+  // (2 workgroups for segment 0, 4 per middle segment: 4-wave scans of 64 columns)
+  // fits the CUs at once, with at least SEG_MIN_CHUNKS chunks per segment on average.
+  const int64_t pairs = static_cast<int64_t>(N) * H;
+  if (N <= 0 || pairs > SEG_MAX_PAIRS || pairs * 8 > cus) return 1;
+  const int64_t avg_chunks = static_cast<int64_t>(T_total) / CHUNK / N;
+  int64_t G = (cus / pairs - 2) / 4 + 2;
+  G = std::min<int64_t>(G, SEG_MAX);
+  G = std::min<int64_t>(G, avg_chunks / SEG_MIN_CHUNKS);
+  return G >= 3 ? static_cast<int>(G) : 1;
+}
+
+hipError_t launch_prefill(const PrefillParams& p_in, int phases, hipStream_t s) {
+  if (p_in.N == 0) return hipSuccess;
   if (phases & PHASE_INTRA) {
-    const hipError_t e = launch_prefill_intra(p, s);
+    const hipError_t e = launch_prefill_intra(p_in, s);
     if (e != hipSuccess) return e;
   }
   if (!(phases & PHASE_SCAN)) return hipSuccess;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  PrefillParams p = p_in;
+  const int64_t pairs = static_cast<int64_t>(p.N) * p.H;
+  p.seg_G = p.seg_ws ? prefill_segments(p.N, p.T_total, p.H, cus) : 1;
+  if (p.seg_G >= 3) {
+    // Segment-parallel scan (phase A: segment 0 and the middle segments' state maps;
+    // combine; phase C: the later segments from their start states).
+    if ((e = launch_scan<4, 4, SCAN_NB, MODE_SEG_A>(p, s)) != hipSuccess) return e;
+    hipLaunchKernelGGL(seg_combine_kernel, dim3(static_cast<unsigned>(pairs * (D / COMB_COLS))),
+                       dim3(256), 0, s, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return launch_scan<2, 2, SCAN_NB, MODE_SEG_C>(p, s);
+  }
   // Two compute waves (32 value columns) per workgroup when the four workgroups of every
   // (sequence, head) pair fit on the chip at once, else four (64 columns): each CU then
   // takes in half as much record per column, which costs a second wave of
   // workgroups when the pairs outnumber a quarter of the CUs (measured on MI355X:
   // 279 vs 320 us at 4x8192 x16 heads, 145 vs 102 us at 8x2048 x16 heads).
-  int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return e;
-  const int64_t pairs = static_cast<int64_t>(p.N) * p.H;
-  if (pairs * 4 <= cus) return launch_scan<2, 2, SCAN_NB>(p, s);
-  return launch_scan<4, 4, SCAN_NB>(p, s);
+  if (pairs * 4 <= cus) return launch_scan<2, 2, SCAN_NB, MODE_SEQ>(p, s);
+  return launch_scan<4, 4, SCAN_NB, MODE_SEQ>(p, s);
 }
 
 }  // namespace kda

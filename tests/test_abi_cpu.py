@@ -34,7 +34,11 @@ def test_abi_version_and_workspace_size(lib):
     rec = 61 * 1024
     # chunk slots = floor(T/64) + N
     assert lib.kda_chunk_prefill_workspace_size(4, 32768, 16, 128) == (512 + 4) * 16 * rec
-    assert lib.kda_chunk_prefill_workspace_size(1, 100, 2, 128) == (1 + 1) * 2 * rec
+    # few (sequence, head) pairs: room for the segment-parallel scan's states as well
+    seg = 19 * 128 * 128 * 4
+    assert lib.kda_chunk_prefill_workspace_size(1, 100, 2, 128) == (1 + 1) * 2 * rec + 2 * seg
+    assert lib.kda_chunk_prefill_workspace_size(2, 640, 16, 128) == (10 + 2) * 16 * rec + 32 * seg
+    assert lib.kda_chunk_prefill_workspace_size(3, 640, 16, 128) == (10 + 3) * 16 * rec
     assert lib.kda_chunk_prefill_workspace_size(1, 100, 2, 64) == 0
     assert lib.kda_chunk_prefill_workspace_size(0, 0, 1, 128) == 0
 

@@ -251,3 +251,45 @@ def test_prefill_full_size_sampled(case, heads, seqs):
     if out is not None:
         assert o.data_ptr() == out.data_ptr()
     _compare(data, o, fin, heads=heads, seqs=seqs)
+
+
+# ---------------------------------------------------------------- segment-parallel scan
+# Few (sequence, head) pairs with long sequences take the segment-parallel scan: each
+# segment's state map and offset from a zero start, a combine, then the later segments
+# from their start states.  These shapes force it (2 heads leave most CUs idle) with
+# ragged tails, empty segments of a short sequence, gathered and out-of-pool starts.
+
+@pytest.mark.parametrize("lens,H,init", [
+    ([64 * 40 + 17], 2, "per_seq"),
+    ([3000, 100, 1500], 2, "pool"),
+    ([64 * 33, 64 * 12], 1, None),
+])
+def test_prefill_segmented_scan(lens, H, init):
+    case = W.PrefillCase(f"seg_{len(lens)}x{H}", lens, H, init=init, pool_slots=5,
+                         seed=3200 + sum(lens) % 97)
+    print(f"case {case.name} lens {lens} seed {case.seed}", flush=True)
+    data = W.make_prefill(case)
+    if init == "pool":
+        data["initial_state_idx"][1] = -1          # a sequence starting from zero
+    d = _dev(data)
+    out, fin = _call(d)
+    torch.cuda.synchronize()
+    _compare(data, out, fin)
+
+
+def test_prefill_segmented_scan_scatter_and_in_place_final():
+    case = W.PrefillCase("seg_scatter", [64 * 40 + 17], 2, init="per_seq", seed=3210)
+    data = W.make_prefill(case)
+    d = _dev(data)
+    T, H = d["q"].shape[:2]
+    plain, fin_plain = _call(d)
+    R = T + 9
+    idx = torch.from_numpy(np.random.default_rng(3211).permutation(R)[:T].astype(np.int32)).cuda()
+    out = torch.zeros((R, H, 128), dtype=torch.bfloat16, device="cuda")
+    state = d["initial_state"].clone()
+    chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta_logits"], d["A_log"], d["dt_bias"],
+                  d["lower_bound"], d["cu_seqlens"], initial_state=state, out=out,
+                  final_state=state, scale=d["scale"], out_token_index=idx)
+    torch.cuda.synchronize()
+    assert torch.equal(out[idx.long()].view(torch.int16).cpu(), plain.view(torch.int16).cpu())
+    assert torch.equal(state.cpu(), fin_plain.cpu())
