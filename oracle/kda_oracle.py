@@ -27,6 +27,9 @@ What it computes (the plain definition, token by token, in float64):
   buffer; the pool stays read-only.  Reading used: row t holds the state after
   token t (0-based), so the last row is the all-accepted state.
 
+* Gated output norm -- SGLang PR #42489 "Improve GLM-5.3-Flash DFlash decoding
+  on B300": a sigmoid RMSNorm over D = 128 rows with output and rstd parity.
+  Reading used: y = x / sqrt(mean(x^2) + eps) * weight * sigmoid(gate).
 * Mixed speculative step and commit -- vLLM PR #55737, the "...code steps too"
   commit message: outputs of the prefill segment and of the spec tokens are
   scattered into one layer output by their token indices, and spec rows keep
@@ -247,3 +250,22 @@ def commit_accepted(state_pool, intermediate, state_idx, num_accepted):
         if 0 <= s < pool.shape[0] and 1 <= n <= T:
             pool[s] = inter[b, n - 1]
     return pool
+
+
+# ---------------------------------------------------------------------------
+# Output-gate sigmoid RMSNorm (SGLang PR #42489 "Improve GLM-5.3-Flash DFlash
+# decoding on B300", "Modifications" and "Accuracy Tests": the sigmoid RMSNorm
+# dispatch for bf16, D = 128 rows, checked for output and rstd parity; the page
+# never writes the formula).  Reading used: per row of D channels (one token and
+# head), y = x / sqrt(mean(x^2) + eps) * weight * sigmoid(gate), and rstd is the
+# row's 1 / sqrt(mean(x^2) + eps).
+# ---------------------------------------------------------------------------
+
+def gated_rmsnorm(x, gate, weight, eps):
+    """Returns (y, rstd) in float64 for x, gate [..., D] and weight [D]."""
+    x = np.asarray(x, dtype=np.float64)
+    gate = np.asarray(gate, dtype=np.float64)
+    w = np.asarray(weight, dtype=np.float64)
+    rstd = 1.0 / np.sqrt(np.mean(x * x, axis=-1) + eps)
+    y = x * rstd[..., None] * w * sigmoid(gate)
+    return y, rstd
