@@ -37,7 +37,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from linear_attention_rule_amd import (chunk_prefill, commit_accepted,  # noqa: E402
-                                       prefill_workspace_bytes, recurrent_verify)
+                                       gated_rmsnorm, prefill_workspace_bytes,
+                                       recurrent_verify)
 from linear_attention_rule_amd import workloads as W  # noqa: E402
 
 METRIC = "KDA prefill µs/layer & tokens/s (8192x4, H=16, d=128); verify µs/layer"
@@ -92,6 +93,7 @@ KERNEL_SOURCES = {
     "kda_verify": ("linear_attention_rule_amd/csrc/kda_verify.hip",),
     "kda_commit": ("linear_attention_rule_amd/csrc/kda_commit.hip",),
     "kda_seg_combine": ("linear_attention_rule_amd/csrc/kda_prefill_scan.hip",),
+    "kda_gated_rmsnorm": ("linear_attention_rule_amd/csrc/kda_norm.hip",),
 }
 # rocprofv3 kernel names -> the names used in this benchmark.
 KERNEL_PATTERNS = {
@@ -100,6 +102,7 @@ KERNEL_PATTERNS = {
     "kda_verify": "verify_kernel",
     "kda_commit": "commit_kernel",
     "kda_seg_combine": "seg_combine_kernel",
+    "kda_gated_rmsnorm": "gated_rmsnorm_kernel",
 }
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 CALIB_BYTES = 1 << 30
@@ -128,8 +131,8 @@ def stored_traffic(kernel, workload):
 
 
 MAIN_WORKLOAD = f"prefill {W.LONG.name} + verify {W.VERIFY.name}"
-EXTRAS_WORKLOAD = (f"commit after {W.VERIFY.name} + segmented prefill {W.SINGLE_LONG.name} "
-                   f"+ mixed step {W.MIXED.name}")
+EXTRAS_WORKLOAD = (f"commit after {W.VERIFY.name} + gated norm {W.NORM.name} + segmented "
+                   f"prefill {W.SINGLE_LONG.name} + mixed step {W.MIXED.name}")
 
 
 def targs(kernel_name):
@@ -322,11 +325,24 @@ def bench_next_rows(iters):
     tokens = Tp + Bs * Ts
     mixed_bytes = (tokens * Hm * BYTES_PER_TOKEN_HEAD + Np * Hm * STATE_BYTES
                    + Bs * Hm * STATE_BYTES * (1 + Ts))
+    nd = W.make_norm(W.NORM)
+    nx, ng, nw = nd["x"].cuda(), nd["gate"].cuda(), nd["weight"].cuda()
+    ny = torch.empty_like(nx)
+    nr = torch.empty(nx.shape[:2], dtype=torch.float32, device="cuda")
+    t_norm = time_calls(lambda: gated_rmsnorm(nx, ng, nw, nd["eps"], out=ny, rstd=nr), iters)
+    norm_rows = nx.shape[0] * nx.shape[1]
+    norm_bytes = norm_rows * (3 * 2 * D + 4)
+    rl_norm = roofline(norm_bytes, 0, t_norm)
+    rl_norm["traffic"] = stored_traffic("kda_gated_rmsnorm", EXTRAS_WORKLOAD)
+    del nx, ng, ny, nr
+
     rl_commit = roofline(commit_bytes, 0, t_commit)
     rl_commit["traffic"] = stored_traffic("kda_commit", EXTRAS_WORKLOAD)
     return {
         "commit": {"workload": f"commit after {vcase.name}", "us": round(t_commit * 1e6, 2),
                    "roofline": rl_commit, "algorithmic_bytes": commit_bytes},
+        "gated_rmsnorm": {"workload": W.NORM.name, "us": round(t_norm * 1e6, 2),
+                          "roofline": rl_norm, "algorithmic_bytes": norm_bytes},
         "segmented_prefill": {"workload": sc.name, "us": round(t_single * 1e6, 2),
                               "intra_us": round(t_s_intra * 1e6, 2),
                               "scan_us": round(t_s_scan * 1e6, 2),

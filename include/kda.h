@@ -200,6 +200,28 @@ kda_status kda_commit_accepted(const float* intermediate_state, const int32_t* s
                                const int32_t* num_accepted, float* state_pool,
                                const kda_commit_desc* desc, void* stream);
 
+typedef struct kda_norm_desc {
+  int32_t tokens;            /* rows of x, gate and y */
+  int32_t num_heads;         /* H: each token holds H rows of head_dim channels */
+  int32_t head_dim;          /* must be 128 */
+  float eps;                 /* added to mean(x^2); finite and >= 0 */
+  int64_t x_token_stride, gate_token_stride, y_token_stride;   /* elements, 0 = H*128 */
+} kda_norm_desc;
+
+/*
+ * Output-gate sigmoid RMSNorm (SGLang PR #42489 "Improve GLM-5.3-Flash DFlash decoding
+ * on B300": the sigmoid RMSNorm of bf16, D = 128 rows, checked for output and rstd).
+ * Per row of 128 channels (token t, head h):
+ *     rstd = 1 / sqrt(mean(x^2) + eps),   y = x * rstd * weight * sigmoid(gate)
+ *   x, gate         bf16 [tokens, H, 128] (token-strided)
+ *   weight          fp32 [128], shared by the heads
+ *   y               bf16 [tokens, H, 128]; may be x itself (same pointer and stride),
+ *                   must not overlap gate
+ *   rstd            fp32 [tokens, H] or NULL (not written)
+ */
+kda_status kda_gated_rmsnorm(const void* x, const void* gate, const float* weight, void* y,
+                             float* rstd, const kda_norm_desc* desc, void* stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* kda_last_error(void);
 

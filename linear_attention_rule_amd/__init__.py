@@ -7,8 +7,9 @@ All calls run entirely in the HIP kernels of libkda.so (built in-tree by
 """
 
 from ._binding import (KDAError, chunk_prefill, commit_accepted, default_scale,  # noqa: F401
-                       header_entry_points, load_library, prefill_workspace_bytes,
-                       recurrent_verify)
+                       gated_rmsnorm, header_entry_points, load_library,
+                       prefill_workspace_bytes, recurrent_verify)
 
-__all__ = ["chunk_prefill", "recurrent_verify", "commit_accepted", "load_library",
-           "prefill_workspace_bytes", "KDAError", "default_scale", "header_entry_points"]
+__all__ = ["chunk_prefill", "recurrent_verify", "commit_accepted", "gated_rmsnorm",
+           "load_library", "prefill_workspace_bytes", "KDAError", "default_scale",
+           "header_entry_points"]

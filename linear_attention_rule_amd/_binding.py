@@ -52,6 +52,13 @@ class CommitDesc(ctypes.Structure):
                 ("num_slots", ctypes.c_int32)]
 
 
+class NormDesc(ctypes.Structure):
+    _fields_ = [("tokens", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("eps", ctypes.c_float),
+                ("x_token_stride", ctypes.c_int64), ("gate_token_stride", ctypes.c_int64),
+                ("y_token_stride", ctypes.c_int64)]
+
+
 ABI_VERSION = 2
 _lib = None
 
@@ -89,6 +96,8 @@ def load_library(path: str | None = None):
                                          ctypes.POINTER(VerifyDesc), vp]
     lib.kda_commit_accepted.restype = ctypes.c_int
     lib.kda_commit_accepted.argtypes = [vp, vp, vp, vp, ctypes.POINTER(CommitDesc), vp]
+    lib.kda_gated_rmsnorm.restype = ctypes.c_int
+    lib.kda_gated_rmsnorm.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(NormDesc), vp]
     if lib.kda_abi_version() != ABI_VERSION:
         raise RuntimeError(f"libkda ABI version {lib.kda_abi_version()}, binding expects "
                            f"{ABI_VERSION}")
@@ -304,6 +313,36 @@ def commit_accepted(intermediate, state_idx, num_accepted, state_pool):
                                  _stream_handle(intermediate.device))
     _check(st)
     return state_pool
+
+
+def gated_rmsnorm(x, gate, weight, eps, *, out=None, rstd=None, want_rstd=True):
+    """Output-gate sigmoid RMSNorm over rows of 128 channels.  Returns (y, rstd or None).
+
+    x, gate: bf16 [T, H, 128] (token stride free, heads dense); weight: f32 [128].
+    out may be x itself (in place).
+    """
+    lib = load_library()
+    T, H = int(x.shape[0]), int(x.shape[1])
+    xs = _token_tensor("x", x, H, HEAD_DIM)
+    gs = _token_tensor("gate", gate, H, HEAD_DIM)
+    if gate.shape[0] != T:
+        raise ValueError("gate must have as many tokens as x")
+    _f32("weight", weight, (HEAD_DIM,))
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, H, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+    ys = _token_tensor("out", out, H, HEAD_DIM)
+    if out.shape[0] != T:
+        raise ValueError("out must have as many tokens as x")
+    if rstd is None and want_rstd:
+        rstd = torch.empty((T, H), dtype=torch.float32, device=dev)
+    if rstd is not None:
+        _f32("rstd", rstd, (T, H))
+    desc = NormDesc(T, H, HEAD_DIM, float(eps), xs, gs, ys)
+    st = lib.kda_gated_rmsnorm(_ptr(x), _ptr(gate), _ptr(weight), _ptr(out), _ptr(rstd),
+                               ctypes.byref(desc), _stream_handle(dev))
+    _check(st)
+    return out, rstd
 
 
 def default_scale() -> float:

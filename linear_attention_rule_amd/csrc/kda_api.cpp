@@ -46,6 +46,22 @@ Span span_of(const void* base, int64_t tokens, int64_t stride, int64_t row_elems
 
 bool overlaps(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
 
+// Whether two token-strided tensors of `tokens` rows share a byte.  With equal strides
+// the rows of one sit at a fixed offset from the rows of the other, so interleaved
+// views of one fused buffer are told apart exactly; otherwise the byte spans decide.
+bool rows_overlap(const void* a, const void* b, int64_t tokens, int64_t stride, int64_t b_stride,
+                  int64_t row_elems, int64_t esize) {
+  const Span sa = span_of(a, tokens, stride, row_elems, esize);
+  const Span sb = span_of(b, tokens, b_stride, row_elems, esize);
+  if (!overlaps(sa, sb)) return false;
+  if (stride != b_stride) return true;
+  const int64_t period = stride * esize, width = row_elems * esize;
+  const int64_t d = static_cast<int64_t>(reinterpret_cast<uintptr_t>(b)) -
+                    static_cast<int64_t>(reinterpret_cast<uintptr_t>(a));
+  const int64_t m = ((d % period) + period) % period;   // offset of b's rows past a's
+  return m < width || m > period - width;
+}
+
 // Validates one token-strided bf16 input: returns the effective stride (0 -> dense default).
 kda_status check_stride(const char* name, int64_t stride, int64_t dense, int64_t row_elems,
                         int64_t* eff) {
@@ -298,6 +314,55 @@ kda_status kda_recurrent_verify(const void* q, const void* k, const void* v, con
   p.q_st = qs; p.k_st = ks; p.v_st = vs; p.g_st = gs; p.b_st = bs; p.o_st = os;
   const hipError_t e = kda::launch_verify(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "verify launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+kda_status kda_gated_rmsnorm(const void* x, const void* gate, const float* weight, void* y,
+                             float* rstd, const kda_norm_desc* desc, void* stream) {
+  if (!desc) return fail(KDA_ERR_INVALID_ARGUMENT, "desc is NULL");
+  const int T = desc->tokens, H = desc->num_heads;
+  if (desc->head_dim != KDA_HEAD_DIM)
+    return fail(KDA_ERR_UNSUPPORTED, "head_dim %d unsupported (only 128)", desc->head_dim);
+  if (T < 0 || H < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "bad sizes tokens=%d H=%d", T, H);
+  if (!std::isfinite(desc->eps) || desc->eps < 0.f)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+  const int64_t HD = static_cast<int64_t>(H) * KDA_HEAD_DIM;
+  int64_t xs, gs, ys;
+  if (kda_status s = check_stride("x", desc->x_token_stride, HD, HD, &xs)) return s;
+  if (kda_status s = check_stride("gate", desc->gate_token_stride, HD, HD, &gs)) return s;
+  if (kda_status s = check_stride("y", desc->y_token_stride, HD, HD, &ys)) return s;
+  if (T == 0) return ok();
+  if (!x || !gate || !weight || !y)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "x / gate / weight / y is NULL");
+  if (!aligned16(x) || !aligned16(gate) || !aligned16(weight) || !aligned16(y))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "x / gate / weight / y must be 16-byte aligned");
+  if ((xs | gs | ys) & 7)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "token strides must be multiples of 8");
+  if (rstd && (reinterpret_cast<uintptr_t>(rstd) & 3u))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "rstd must be 4-byte aligned");
+  const Span sy = span_of(y, T, ys, HD, 2);
+  if (rows_overlap(y, gate, T, ys, gs, HD, 2))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "y overlaps gate");
+  if (rows_overlap(y, x, T, ys, xs, HD, 2) && !(y == x && ys == xs))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "y overlaps x (only y == x with equal strides is allowed)");
+  if (rstd && overlaps(span_of(rstd, static_cast<int64_t>(T) * H, 1, 1, 4), sy))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "rstd overlaps y");
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "device query failed: %s", hipGetErrorString(e));
+  kda::NormParams p{};
+  p.x = static_cast<const uint16_t*>(x);
+  p.gate = static_cast<const uint16_t*>(gate);
+  p.weight = weight;
+  p.y = static_cast<uint16_t*>(y);
+  p.rstd = rstd;
+  p.eps = desc->eps;
+  p.tokens = T;
+  p.H = H;
+  p.x_st = xs; p.g_st = gs; p.y_st = ys;
+  e = kda::launch_gated_rmsnorm(p, cus, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "norm launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -5,6 +5,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <stdint.h>
 
 namespace kda {
@@ -59,6 +61,17 @@ struct VerifyParams {
   int64_t q_st, k_st, v_st, g_st, b_st, o_st;
 };
 
+struct NormParams {
+  const uint16_t* x;
+  const uint16_t* gate;
+  const float* weight;
+  uint16_t* y;
+  float* rstd;
+  float eps;
+  int tokens, H;
+  int64_t x_st, g_st, y_st;
+};
+
 struct CommitParams {
   const float* inter;
   const int32_t* idx;
@@ -107,6 +120,7 @@ inline int64_t chunk_slots(int N, int T_total) { return static_cast<int64_t>(T_t
 // Launchers (enqueue only; return the hipGetLastError() of the launch).
 hipError_t launch_verify(const VerifyParams& p, hipStream_t s);
 hipError_t launch_commit(const CommitParams& p, hipStream_t s);
+hipError_t launch_gated_rmsnorm(const NormParams& p, int cus, hipStream_t s);
 // Prefill phases: bit 0 = intra-chunk kernel, bit 1 = state-scan kernel.
 constexpr int PHASE_INTRA = 1;
 constexpr int PHASE_SCAN = 2;

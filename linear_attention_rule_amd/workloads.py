@@ -151,6 +151,30 @@ def make_verify(case: VerifyCase):
                 lower_bound=case.lower_bound, scale=1.0 / math.sqrt(D))
 
 
+@dataclass
+class NormCase:
+    name: str
+    tokens: int
+    heads: int
+    eps: float = 1e-6
+    seed: int = 1009
+    head_dim: int = HEAD_DIM
+
+
+# The gated output norm at the size of the 4 x 8192 prefill output (16 heads).
+NORM = NormCase("gated_norm_32768x16", 32768, 16, seed=1009)
+
+
+def make_norm(case: NormCase):
+    """x, gate bf16 [T, H, D] ~ N(0, 1); weight f32 [D] ~ U(0.5, 1.5)."""
+    rng = np.random.default_rng(case.seed)
+    T, H, D = case.tokens, case.heads, case.head_dim
+    x = _bf16(rng, (T, H, D))
+    gate = _bf16(rng, (T, H, D))
+    weight = torch.from_numpy(rng.uniform(0.5, 1.5, size=D).astype(np.float32))
+    return dict(x=x, gate=gate, weight=weight, eps=case.eps)
+
+
 def make_mixed(case: MixedCase):
     """Draw one mixed step: the prefill and spec workloads, the token order of the merged
     layer output (non_spec_idx [T_prefill], spec_idx [B*T], int32, disjoint), the output

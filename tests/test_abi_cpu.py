@@ -24,7 +24,7 @@ def test_exports_every_declared_symbol(lib):
     names = L.header_entry_points()
     assert set(names) >= {"kda_chunk_prefill", "kda_recurrent_verify", "kda_last_error",
                           "kda_abi_version", "kda_chunk_prefill_workspace_size",
-                          "kda_commit_accepted"}
+                          "kda_commit_accepted", "kda_gated_rmsnorm"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -156,3 +156,40 @@ def test_commit_rejects_bad_arguments(lib):
     assert b"overlap" in lib.kda_last_error()
     assert lib.kda_commit_accepted(_fake(40), _fake(7), _fake(8), _fake(20), None, None) == INVALID
     assert _commit(lib, _cdesc(Bn=0)) == KDA_OK
+
+
+def _ndesc(T=4, H=2, D=128, eps=1e-6):
+    return B.NormDesc(T, H, D, eps, 0, 0, 0)
+
+
+def _norm(lib, desc, x=None, gate=None, y=None):
+    f = _fake
+    return lib.kda_gated_rmsnorm(x if x is not None else f(1), gate if gate is not None else f(2),
+                                 f(3), y if y is not None else f(4), None, ctypes.byref(desc), None)
+
+
+def test_norm_rejects_bad_arguments(lib):
+    assert _norm(lib, _ndesc(D=64)) == UNSUPPORTED
+    assert _norm(lib, _ndesc(eps=-1.0)) == INVALID
+    assert _norm(lib, _ndesc(eps=float("inf"))) == INVALID
+    assert _norm(lib, _ndesc(H=0)) == INVALID
+    assert _norm(lib, _ndesc(), y=_fake(2)) == INVALID          # y over gate
+    assert b"gate" in lib.kda_last_error()
+    d = _ndesc()
+    d.y_token_stride = 512                                     # y == x but another stride
+    assert _norm(lib, d, y=_fake(1)) == INVALID
+    assert _norm(lib, _ndesc(T=0)) == KDA_OK
+
+
+def test_norm_accepts_interleaved_views(lib):
+    # x and gate interleaved rows of one fused buffer (stride 3*H*128), y in place over x:
+    # validation passes (without a GPU the call then fails at the device query).
+    d = _ndesc(T=4, H=2)
+    d.x_token_stride = d.gate_token_stride = d.y_token_stride = 3 * 2 * 128
+    st = _norm(lib, d, x=_fake(1), gate=ctypes.c_void_p(0x10000 + 2 * 128 * 2), y=_fake(1))
+    assert st not in (INVALID, UNSUPPORTED), lib.kda_last_error()
+    # gate one row later than x (same stride) still overlaps
+    d2 = _ndesc(T=4, H=2)
+    d2.x_token_stride = d2.gate_token_stride = d2.y_token_stride = 2 * 2 * 128
+    st = _norm(lib, d2, x=_fake(1), gate=ctypes.c_void_p(0x10000 + 100), y=_fake(1))
+    assert st == INVALID
