@@ -27,6 +27,9 @@ What it computes (the plain definition, token by token, in float64):
   buffer; the pool stays read-only.  Reading used: row t holds the state after
   token t (0-based), so the last row is the all-accepted state.
 
+* Short causal conv -- TensorRT-LLM PR #21179 (fused-verify commit message) and vLLM
+  PR #55737 ("Notes for review"): depthwise causal conv of width W <= 4 per channel
+  with optional bias and SiLU, windows of the W-1 previous inputs.
 * Gated output norm -- SGLang PR #42489 "Improve GLM-5.3-Flash DFlash decoding
   on B300": a sigmoid RMSNorm over D = 128 rows with output and rstd parity.
   Reading used: y = x / sqrt(mean(x^2) + eps) * weight * sigmoid(gate).
@@ -269,3 +272,85 @@ def gated_rmsnorm(x, gate, weight, eps):
     rstd = 1.0 / np.sqrt(np.mean(x * x, axis=-1) + eps)
     y = x * rstd[..., None] * w * sigmoid(gate)
     return y, rstd
+
+
+# ---------------------------------------------------------------------------
+# Short causal convolution on the q / k / v projections (TensorRT-LLM PR #21179,
+# fused-verify commit message: three short convolutions per draft step, run as
+# one packed causal_conv1d_update that writes each step's window into
+# intermediate_conv_window from a gathered copy of the pool rows, inputs read
+# in place from the fused projection; vLLM PR #55737, "Notes for review": the
+# short conv per q/k/v into separate buffers).  Readings used: a depthwise causal
+# convolution of width W <= 4 per channel c,
+#     y_t[c] = act(bias[c] + sum_{i<W} weight[c, i] * x_{t-W+1+i}[c]),
+# where inputs before a sequence's first token come from its window (the W-1
+# previous inputs, oldest first; zeros when the window index is out of range),
+# act is SiLU (x * sigmoid(x)) or the identity, and the window after a token is
+# the last W-1 inputs up to and including it.
+# ---------------------------------------------------------------------------
+
+def _conv_run(xs, window, weight, bias, silu):
+    """Token loop over one sequence.  xs [L, C], window [W-1, C] -> (y [L, C], windows
+    [L, W-1, C] after each token)."""
+    W = weight.shape[1]
+    hist = [window[i] for i in range(W - 1)]
+    ys, wins = [], []
+    for t in range(xs.shape[0]):
+        taps = hist + [xs[t]]                       # oldest first, W entries
+        acc = np.zeros(xs.shape[1]) if bias is None else np.array(bias, dtype=np.float64)
+        for i in range(W):
+            acc = acc + weight[:, i] * taps[i]
+        ys.append(acc * sigmoid(acc) if silu else acc)
+        hist = taps[1:]
+        wins.append(np.stack(hist) if W > 1 else np.zeros((0, xs.shape[1])))
+    y = np.stack(ys) if ys else np.zeros((0, xs.shape[1]))
+    win = np.stack(wins) if wins else np.zeros((0, W - 1, xs.shape[1]))
+    return y, win
+
+
+def conv1d_prefill(x, weight, bias, cu_seqlens, state, state_idx, silu=True):
+    """Varlen causal conv.  x [T, C]; weight [C, W]; bias [C] or None; state [slots, W-1, C]
+    (windows, or None for zeros); state_idx [N] or None (row n).  Returns (y [T, C],
+    new_state [slots, W-1, C]: each in-range indexed window replaced by the window after
+    its sequence)."""
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(weight, dtype=np.float64)
+    W = w.shape[1]
+    C = x.shape[1]
+    cu = [int(v) for v in np.asarray(cu_seqlens).reshape(-1)]
+    y = np.zeros_like(x)
+    new_state = None if state is None else np.array(state, dtype=np.float64, copy=True)
+    for n in range(len(cu) - 1):
+        row = n if state_idx is None else int(np.asarray(state_idx).reshape(-1)[n])
+        in_pool = state is not None and 0 <= row < state.shape[0]
+        win0 = (np.asarray(state[row], dtype=np.float64) if in_pool else np.zeros((W - 1, C)))
+        ys, wins = _conv_run(x[cu[n]:cu[n + 1]], win0, w, bias, silu)
+        y[cu[n]:cu[n + 1]] = ys
+        if in_pool and len(ys):
+            new_state[row] = wins[-1]
+    return y, new_state
+
+
+def conv1d_update(x, weight, bias, state_pool, state_idx, num_steps, silu=True):
+    """Multi-step update: B rows of T tokens (token b*T + t) from pool windows (read only).
+    Returns (y [B*T, C], intermediate [B, T, W-1, C]: the window after token t).  A row whose
+    index lies outside the pool is padding: zero outputs and zero windows (the GPU leaves
+    its windows unwritten)."""
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(weight, dtype=np.float64)
+    W = w.shape[1]
+    T = int(num_steps)
+    B = x.shape[0] // T
+    C = x.shape[1]
+    y = np.zeros_like(x)
+    inter = np.zeros((B, T, W - 1, C))
+    idx = np.asarray(state_idx).reshape(-1)
+    for b in range(B):
+        s = int(idx[b])
+        if not 0 <= s < state_pool.shape[0]:
+            continue
+        ys, wins = _conv_run(x[b * T:(b + 1) * T], np.asarray(state_pool[s], np.float64), w, bias,
+                             silu)
+        y[b * T:(b + 1) * T] = ys
+        inter[b] = wins
+    return y, inter
