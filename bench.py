@@ -36,7 +36,8 @@ import torch
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from linear_attention_rule_amd import (chunk_prefill, commit_accepted,  # noqa: E402
+from linear_attention_rule_amd import (causal_conv1d_prefill,  # noqa: E402
+                                       causal_conv1d_update, chunk_prefill, commit_accepted,
                                        gated_rmsnorm, prefill_workspace_bytes,
                                        recurrent_verify)
 from linear_attention_rule_amd import workloads as W  # noqa: E402
@@ -94,6 +95,9 @@ KERNEL_SOURCES = {
     "kda_commit": ("linear_attention_rule_amd/csrc/kda_commit.hip",),
     "kda_seg_combine": ("linear_attention_rule_amd/csrc/kda_prefill_scan.hip",),
     "kda_gated_rmsnorm": ("linear_attention_rule_amd/csrc/kda_norm.hip",),
+    "kda_conv_prefill": ("linear_attention_rule_amd/csrc/kda_conv.hip",),
+    "kda_conv_state": ("linear_attention_rule_amd/csrc/kda_conv.hip",),
+    "kda_conv_update": ("linear_attention_rule_amd/csrc/kda_conv.hip",),
 }
 # rocprofv3 kernel names -> the names used in this benchmark.
 KERNEL_PATTERNS = {
@@ -103,6 +107,9 @@ KERNEL_PATTERNS = {
     "kda_commit": "commit_kernel",
     "kda_seg_combine": "seg_combine_kernel",
     "kda_gated_rmsnorm": "gated_rmsnorm_kernel",
+    "kda_conv_prefill": "conv_prefill_kernel",
+    "kda_conv_state": "conv_state_kernel",
+    "kda_conv_update": "conv_update_kernel",
 }
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 CALIB_BYTES = 1 << 30
@@ -131,8 +138,9 @@ def stored_traffic(kernel, workload):
 
 
 MAIN_WORKLOAD = f"prefill {W.LONG.name} + verify {W.VERIFY.name}"
-EXTRAS_WORKLOAD = (f"commit after {W.VERIFY.name} + gated norm {W.NORM.name} + segmented "
-                   f"prefill {W.SINGLE_LONG.name} + mixed step {W.MIXED.name}")
+EXTRAS_WORKLOAD = (f"commit after {W.VERIFY.name} + conv {W.CONV_PREFILL.name} / "
+                   f"{W.CONV_UPDATE.name} + gated norm {W.NORM.name} + segmented prefill "
+                   f"{W.SINGLE_LONG.name} + mixed step {W.MIXED.name}")
 
 
 def targs(kernel_name):
@@ -336,11 +344,42 @@ def bench_next_rows(iters):
     rl_norm["traffic"] = stored_traffic("kda_gated_rmsnorm", EXTRAS_WORKLOAD)
     del nx, ng, ny, nr
 
+    # Short conv on the packed q|k|v columns: prefill at 4 x 8192, update at 64 x 8.
+    cp = W.make_conv(W.CONV_PREFILL)
+    cx, cw, cb = cp["x"].cuda(), cp["weight"].cuda(), cp["bias"].cuda()
+    cst, cidx, ccu = cp["state"].cuda(), cp["state_idx"].cuda(), cp["cu_seqlens"].cuda()
+    cy = torch.empty_like(cx)
+    t_convp = time_calls(lambda: causal_conv1d_prefill(cx, cw, cb, ccu, conv_state=cst,
+                                                       state_idx=cidx, out=cy), iters)
+    Tc, Cc = cx.shape
+    Wc = W.CONV_PREFILL.width
+    Nc = ccu.numel() - 1
+    convp_bytes = 2 * Tc * Cc * 2 + 2 * Nc * (Wc - 1) * Cc * 2 + Cc * (Wc + 1) * 2
+    del cx, cy, cst
+    cu_ = W.make_conv(W.CONV_UPDATE)
+    ux, uw, ub = cu_["x"].cuda(), cu_["weight"].cuda(), cu_["bias"].cuda()
+    upool, uidx = cu_["state"].cuda(), cu_["state_idx"].cuda()
+    Bu, Tu = W.CONV_UPDATE.batch, W.CONV_UPDATE.steps
+    uy = torch.empty_like(ux)
+    uint = torch.empty((Bu, Tu, Wc - 1, Cc), dtype=torch.bfloat16, device="cuda")
+    t_convu = time_calls(lambda: causal_conv1d_update(ux, uw, ub, upool, uidx, Tu,
+                                                      intermediate=uint, out=uy), iters)
+    convu_bytes = (2 * Bu * Tu * Cc * 2 + Bu * (Wc - 1) * Cc * 2 + Bu * Tu * (Wc - 1) * Cc * 2
+                   + Cc * (Wc + 1) * 2)
+    del ux, uy, upool, uint
+    rl_convp = roofline(convp_bytes, 0, t_convp)
+    rl_convp["traffic"] = stored_traffic("kda_conv_prefill", EXTRAS_WORKLOAD)
+    rl_convu = roofline(convu_bytes, 0, t_convu)
+
     rl_commit = roofline(commit_bytes, 0, t_commit)
     rl_commit["traffic"] = stored_traffic("kda_commit", EXTRAS_WORKLOAD)
     return {
         "commit": {"workload": f"commit after {vcase.name}", "us": round(t_commit * 1e6, 2),
                    "roofline": rl_commit, "algorithmic_bytes": commit_bytes},
+        "conv_prefill": {"workload": W.CONV_PREFILL.name, "us": round(t_convp * 1e6, 2),
+                         "roofline": rl_convp, "algorithmic_bytes": convp_bytes},
+        "conv_update": {"workload": W.CONV_UPDATE.name, "us": round(t_convu * 1e6, 2),
+                        "roofline": rl_convu, "algorithmic_bytes": convu_bytes},
         "gated_rmsnorm": {"workload": W.NORM.name, "us": round(t_norm * 1e6, 2),
                           "roofline": rl_norm, "algorithmic_bytes": norm_bytes},
         "segmented_prefill": {"workload": sc.name, "us": round(t_single * 1e6, 2),

@@ -222,6 +222,52 @@ typedef struct kda_norm_desc {
 kda_status kda_gated_rmsnorm(const void* x, const void* gate, const float* weight, void* y,
                              float* rstd, const kda_norm_desc* desc, void* stream);
 
+typedef struct kda_conv_desc {
+  int32_t num_seqs;          /* prefill: N sequences (cu_seqlens has N+1); update: B rows */
+  int32_t total_tokens;      /* prefill: T_total == cu_seqlens[N]; update: B * num_steps */
+  int32_t num_steps;         /* update: T tokens per row (token b*T + t); prefill: unused */
+  int32_t channels;          /* C, a positive multiple of 8 (3*H*128 for packed q|k|v) */
+  int32_t width;             /* W taps, 1..4 */
+  int32_t num_state_slots;   /* rows of the window pool */
+  int32_t silu;              /* 1: y = SiLU(conv); 0: y = conv */
+  int64_t x_token_stride;    /* elements between tokens of x; 0 = C */
+  int64_t y_token_stride;    /* elements between tokens of y; 0 = C */
+} kda_conv_desc;
+
+/*
+ * Short causal convolution of the q / k / v projections (TensorRT-LLM PR #21179,
+ * fused-verify commit message; vLLM PR #55737, "Notes for review").  Depthwise, per
+ * channel c:  y_t[c] = act(bias[c] + sum_{i<W} weight[c][i] * x_{t-W+1+i}[c]).
+ * A window holds the W-1 inputs before a token, oldest first: bf16 [W-1, C].
+ *
+ * Prefill over N packed sequences:
+ *   x           bf16 [T_total, C] (token-strided: e.g. the q|k|v columns of a fused
+ *               projection); weight bf16 [C, W]; bias bf16 [C] or NULL
+ *   conv_state  bf16 [slots, W-1, C] or NULL (zero windows, nothing written).  Sequence n
+ *               starts from window state_idx[n] (row n when state_idx is NULL; zeros
+ *               for an index outside [0, slots)), and that window is replaced by the
+ *               one after its last token (kept when the sequence is empty).  Two
+ *               sequences must not name one window.
+ *   y           bf16 [T_total, C], token-strided; must not overlap x or conv_state
+ */
+kda_status kda_causal_conv1d_prefill(const void* x, const void* weight, const void* bias,
+                                     const int32_t* cu_seqlens, void* conv_state,
+                                     const int32_t* state_idx, void* y,
+                                     const kda_conv_desc* desc, void* stream);
+
+/*
+ * Multi-step update for verify (the packed causal_conv1d_update of TensorRT-LLM PR
+ * #21179): B rows of T tokens (token b*T + t), each row starting from window
+ * conv_state[state_idx[b]], which is only read.  An index outside [0, slots) marks a
+ * padding row: zero outputs, its windows untouched.
+ *   intermediate_window  bf16 [B, T, W-1, C]: (b, t) receives the window after token t
+ *   y                    bf16 [B*T, C], token-strided
+ */
+kda_status kda_causal_conv1d_update(const void* x, const void* weight, const void* bias,
+                                    const void* conv_state, const int32_t* state_idx,
+                                    void* intermediate_window, void* y,
+                                    const kda_conv_desc* desc, void* stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* kda_last_error(void);
 

@@ -59,6 +59,14 @@ class NormDesc(ctypes.Structure):
                 ("y_token_stride", ctypes.c_int64)]
 
 
+class ConvDesc(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("total_tokens", ctypes.c_int32),
+                ("num_steps", ctypes.c_int32), ("channels", ctypes.c_int32),
+                ("width", ctypes.c_int32), ("num_state_slots", ctypes.c_int32),
+                ("silu", ctypes.c_int32), ("x_token_stride", ctypes.c_int64),
+                ("y_token_stride", ctypes.c_int64)]
+
+
 ABI_VERSION = 2
 _lib = None
 
@@ -96,6 +104,12 @@ def load_library(path: str | None = None):
                                          ctypes.POINTER(VerifyDesc), vp]
     lib.kda_commit_accepted.restype = ctypes.c_int
     lib.kda_commit_accepted.argtypes = [vp, vp, vp, vp, ctypes.POINTER(CommitDesc), vp]
+    lib.kda_causal_conv1d_prefill.restype = ctypes.c_int
+    lib.kda_causal_conv1d_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp,
+                                              ctypes.POINTER(ConvDesc), vp]
+    lib.kda_causal_conv1d_update.restype = ctypes.c_int
+    lib.kda_causal_conv1d_update.argtypes = [vp, vp, vp, vp, vp, vp, vp,
+                                             ctypes.POINTER(ConvDesc), vp]
     lib.kda_gated_rmsnorm.restype = ctypes.c_int
     lib.kda_gated_rmsnorm.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(NormDesc), vp]
     if lib.kda_abi_version() != ABI_VERSION:
@@ -111,7 +125,7 @@ def header_entry_points() -> list[str]:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
     text = re.sub(r"//[^\n]*", " ", text)
-    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(kda_[a-z0-9_]+)\s*\(", text)))
 
 
 def _ptr(t):
@@ -343,6 +357,96 @@ def gated_rmsnorm(x, gate, weight, eps, *, out=None, rstd=None, want_rstd=True):
                                ctypes.byref(desc), _stream_handle(dev))
     _check(st)
     return out, rstd
+
+
+def _rows_tensor(name, t, width):
+    """A bf16 [tokens, width] view with contiguous channels; returns its token stride."""
+    if t.dtype != torch.bfloat16 or not t.is_cuda:
+        raise TypeError(f"{name} must be a bfloat16 device tensor")
+    if t.dim() != 2 or t.shape[1] != width:
+        raise ValueError(f"{name} must be [tokens, {width}]")
+    if t.numel() == 0:
+        return 0
+    if t.stride(1) != 1:
+        raise ValueError(f"{name} must have contiguous channels")
+    return t.stride(0)
+
+
+def _conv_weights(weight, bias, C):
+    if weight.dtype != torch.bfloat16 or not weight.is_cuda or not weight.is_contiguous() \
+            or weight.dim() != 2 or weight.shape[0] != C:
+        raise TypeError(f"weight must be a contiguous bf16 device tensor [{C}, W]")
+    if bias is not None and (bias.dtype != torch.bfloat16 or not bias.is_cuda or
+                             not bias.is_contiguous() or tuple(bias.shape) != (C,)):
+        raise TypeError(f"bias must be a contiguous bf16 device tensor [{C}]")
+    return int(weight.shape[1])
+
+
+def _windows(name, t, W, C, rows=None):
+    if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous bf16 device tensor")
+    if t.shape[-2:] != (W - 1, C) or (rows is not None and t.shape[0] != rows):
+        raise ValueError(f"{name} must be [{rows or 'slots'}, {W - 1}, {C}]")
+
+
+def causal_conv1d_prefill(x, weight, bias, cu_seqlens, *, conv_state=None, state_idx=None,
+                          out=None, silu=True):
+    """Short causal conv over N packed sequences.  Returns y [T, C] (bf16).
+
+    x: bf16 [T, C] (token stride free); weight bf16 [C, W]; bias bf16 [C] or None;
+    conv_state: bf16 [slots, W-1, C] windows, updated in place; state_idx int32 [N] or None.
+    """
+    lib = load_library()
+    T, C = int(x.shape[0]), int(x.shape[1])
+    xs = _rows_tensor("x", x, C)
+    W = _conv_weights(weight, bias, C)
+    _i32("cu_seqlens", cu_seqlens, None)
+    N = int(cu_seqlens.numel()) - 1
+    slots = 0
+    if conv_state is not None:
+        _windows("conv_state", conv_state, W, C)
+        slots = int(conv_state.shape[0])
+    if state_idx is not None:
+        _i32("state_idx", state_idx, N)
+    if out is None:
+        out = torch.empty((T, C), dtype=torch.bfloat16, device=x.device)
+    ys = _rows_tensor("out", out, C)
+    desc = ConvDesc(N, T, 0, C, W, slots, 1 if silu else 0, xs, ys)
+    st = lib.kda_causal_conv1d_prefill(_ptr(x), _ptr(weight), _ptr(bias), _ptr(cu_seqlens),
+                                       _ptr(conv_state), _ptr(state_idx), _ptr(out),
+                                       ctypes.byref(desc), _stream_handle(x.device))
+    _check(st)
+    return out
+
+
+def causal_conv1d_update(x, weight, bias, conv_state, state_idx, num_steps, *,
+                         intermediate=None, out=None, silu=True):
+    """Multi-step conv update for verify.  Returns (y [B*T, C], intermediate [B, T, W-1, C]).
+
+    The pool conv_state [slots, W-1, C] is only read; state_idx int32 [B] (out of range =
+    padding row)."""
+    lib = load_library()
+    BT, C = int(x.shape[0]), int(x.shape[1])
+    T = int(num_steps)
+    if T < 1 or BT % T:
+        raise ValueError("token count must be a multiple of num_steps")
+    B = BT // T
+    xs = _rows_tensor("x", x, C)
+    W = _conv_weights(weight, bias, C)
+    _windows("conv_state", conv_state, W, C)
+    _i32("state_idx", state_idx, B)
+    if intermediate is None:
+        intermediate = torch.empty((B, T, W - 1, C), dtype=torch.bfloat16, device=x.device)
+    _windows("intermediate", intermediate.view(B * T, W - 1, C), W, C, B * T)
+    if out is None:
+        out = torch.empty((BT, C), dtype=torch.bfloat16, device=x.device)
+    ys = _rows_tensor("out", out, C)
+    desc = ConvDesc(B, BT, T, C, W, int(conv_state.shape[0]), 1 if silu else 0, xs, ys)
+    st = lib.kda_causal_conv1d_update(_ptr(x), _ptr(weight), _ptr(bias), _ptr(conv_state),
+                                      _ptr(state_idx), _ptr(intermediate), _ptr(out),
+                                      ctypes.byref(desc), _stream_handle(x.device))
+    _check(st)
+    return out, intermediate
 
 
 def default_scale() -> float:

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkda.so")
 ARCH = "gfx950"
 
-SOURCES = ["kda_api.cpp", "kda_verify.hip", "kda_commit.hip", "kda_norm.hip",
+SOURCES = ["kda_api.cpp", "kda_verify.hip", "kda_commit.hip", "kda_norm.hip", "kda_conv.hip",
            "kda_prefill_intra.hip", "kda_prefill_scan.hip"]
 
 # Per-source additions.  The intra kernel is a chain of short LDS / MFMA phases; the

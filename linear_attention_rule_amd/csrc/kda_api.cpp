@@ -317,6 +317,115 @@ kda_status kda_recurrent_verify(const void* q, const void* k, const void* v, con
   return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+// Host checks shared by the two conv entry points; fills the common fields of p.
+kda_status conv_common(const void* x, const void* weight, const void* bias, const void* y,
+                       const kda_conv_desc* desc, int64_t tokens, kda::ConvParams* p) {
+  const int C = desc->channels, W = desc->width;
+  if (C < 8 || C % 8) return fail(KDA_ERR_INVALID_ARGUMENT, "channels %d: positive multiple of 8", C);
+  if (W < 1 || W > 4) return fail(KDA_ERR_UNSUPPORTED, "width %d outside 1..4", W);
+  if (desc->num_state_slots < 0)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "num_state_slots %d < 0", desc->num_state_slots);
+  int64_t xs, ys;
+  if (kda_status s = check_stride("x", desc->x_token_stride, C, C, &xs)) return s;
+  if (kda_status s = check_stride("y", desc->y_token_stride, C, C, &ys)) return s;
+  if (tokens > 0) {
+    if (!x || !weight || !y) return fail(KDA_ERR_INVALID_ARGUMENT, "x / weight / y is NULL");
+    if (!aligned16(x) || !aligned16(y) || !aligned16(weight) || (bias && !aligned16(bias)))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "x / y / weight / bias must be 16-byte aligned");
+    if ((xs | ys) & 7) return fail(KDA_ERR_INVALID_ARGUMENT, "token strides must be multiples of 8");
+    if (rows_overlap(y, x, tokens, ys, xs, C, 2))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "y overlaps x");
+  }
+  p->x = static_cast<const uint16_t*>(x);
+  p->weight = static_cast<const uint16_t*>(weight);
+  p->bias = static_cast<const uint16_t*>(bias);
+  p->y = static_cast<uint16_t*>(const_cast<void*>(y));
+  p->C = C;
+  p->W = W;
+  p->slots = desc->num_state_slots;
+  p->silu = desc->silu != 0;
+  p->x_st = xs;
+  p->y_st = ys;
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_causal_conv1d_prefill(const void* x, const void* weight, const void* bias,
+                                     const int32_t* cu_seqlens, void* conv_state,
+                                     const int32_t* state_idx, void* y,
+                                     const kda_conv_desc* desc, void* stream) {
+  if (!desc) return fail(KDA_ERR_INVALID_ARGUMENT, "desc is NULL");
+  const int N = desc->num_seqs, T = desc->total_tokens;
+  if (N < 0 || T < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "bad sizes N=%d T_total=%d", N, T);
+  kda::ConvParams p{};
+  if (kda_status s = conv_common(x, weight, bias, y, desc, T, &p)) return s;
+  if (N > 0 && !cu_seqlens) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL");
+  if (conv_state && desc->width > 1) {
+    if (!aligned16(conv_state))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "conv_state must be 16-byte aligned");
+    if (desc->num_state_slots < (state_idx ? 1 : N))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "num_state_slots %d too small", desc->num_state_slots);
+    const int64_t win = static_cast<int64_t>(desc->width - 1) * desc->channels;
+    if (T > 0 && overlaps(span_of(conv_state, desc->num_state_slots, win, win, 2),
+                          span_of(y, T, p.y_st, desc->channels, 2)))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "y overlaps conv_state");
+  }
+  if (N == 0) return ok();
+  p.cu = cu_seqlens;
+  p.state = desc->width > 1 ? static_cast<uint16_t*>(conv_state) : nullptr;
+  p.state_idx = state_idx;
+  p.N = N;
+  p.T_total = T;
+  const hipError_t e = kda::launch_conv_prefill(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "conv launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+kda_status kda_causal_conv1d_update(const void* x, const void* weight, const void* bias,
+                                    const void* conv_state, const int32_t* state_idx,
+                                    void* intermediate_window, void* y,
+                                    const kda_conv_desc* desc, void* stream) {
+  if (!desc) return fail(KDA_ERR_INVALID_ARGUMENT, "desc is NULL");
+  const int B = desc->num_seqs, T = desc->num_steps;
+  if (B < 0 || T < 1 || T > KDA_MAX_VERIFY_STEPS)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "bad sizes B=%d num_steps=%d", B, T);
+  if (static_cast<int64_t>(B) * T != desc->total_tokens)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "total_tokens must be B * num_steps");
+  kda::ConvParams p{};
+  if (kda_status s = conv_common(x, weight, bias, y, desc, static_cast<int64_t>(B) * T, &p))
+    return s;
+  if (B == 0) return ok();
+  if (!state_idx || (desc->width > 1 && (!conv_state || !intermediate_window)))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "state_idx / conv_state / intermediate_window is NULL");
+  if (desc->num_state_slots < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "num_state_slots < 1");
+  if (desc->width > 1) {
+    if (!aligned16(conv_state) || !aligned16(intermediate_window))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "windows must be 16-byte aligned");
+    const int64_t win = static_cast<int64_t>(desc->width - 1) * desc->channels;
+    const Span s_pool = span_of(conv_state, desc->num_state_slots, win, win, 2);
+    const Span s_int = span_of(intermediate_window, static_cast<int64_t>(B) * T, win, win, 2);
+    const Span s_y = span_of(y, static_cast<int64_t>(B) * T, p.y_st, desc->channels, 2);
+    if (overlaps(s_pool, s_int) || overlaps(s_y, s_int) || overlaps(s_y, s_pool))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "windows overlap each other or y");
+  }
+  p.state = const_cast<uint16_t*>(static_cast<const uint16_t*>(conv_state));
+  p.state_idx = state_idx;
+  p.inter = static_cast<uint16_t*>(intermediate_window);
+  p.N = B;
+  p.T = T;
+  p.T_total = B * T;
+  const hipError_t e = kda::launch_conv_update(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "conv launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 kda_status kda_gated_rmsnorm(const void* x, const void* gate, const float* weight, void* y,
                              float* rstd, const kda_norm_desc* desc, void* stream) {
   if (!desc) return fail(KDA_ERR_INVALID_ARGUMENT, "desc is NULL");

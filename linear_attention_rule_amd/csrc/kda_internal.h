@@ -72,6 +72,20 @@ struct NormParams {
   int64_t x_st, g_st, y_st;
 };
 
+struct ConvParams {
+  const uint16_t* x;
+  const uint16_t* weight;    // [C, W] bf16
+  const uint16_t* bias;      // [C] bf16 or null
+  const int32_t* cu;         // prefill: cu_seqlens
+  uint16_t* state;           // windows [slots, W-1, C] (prefill: updated; update: read only)
+  const int32_t* state_idx;
+  uint16_t* inter;           // update: windows after each token [B, T, W-1, C]
+  uint16_t* y;
+  int N, T_total, T, C, W, slots;
+  bool silu;
+  int64_t x_st, y_st;
+};
+
 struct CommitParams {
   const float* inter;
   const int32_t* idx;
@@ -121,6 +135,8 @@ inline int64_t chunk_slots(int N, int T_total) { return static_cast<int64_t>(T_t
 hipError_t launch_verify(const VerifyParams& p, hipStream_t s);
 hipError_t launch_commit(const CommitParams& p, hipStream_t s);
 hipError_t launch_gated_rmsnorm(const NormParams& p, int cus, hipStream_t s);
+hipError_t launch_conv_prefill(const ConvParams& p, hipStream_t s);
+hipError_t launch_conv_update(const ConvParams& p, hipStream_t s);
 // Prefill phases: bit 0 = intra-chunk kernel, bit 1 = state-scan kernel.
 constexpr int PHASE_INTRA = 1;
 constexpr int PHASE_SCAN = 2;

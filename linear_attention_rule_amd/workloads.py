@@ -175,6 +175,53 @@ def make_norm(case: NormCase):
     return dict(x=x, gate=gate, weight=weight, eps=case.eps)
 
 
+@dataclass
+class ConvCase:
+    name: str
+    seq_lens: list                 # prefill: sequence lengths; update: ignored
+    channels: int
+    width: int = 4
+    pool_slots: int = 0            # windows in the pool (0: no windows)
+    batch: int = 0                 # update: B rows
+    steps: int = 0                 # update: T tokens per row
+    bias: bool = True
+    seed: int = 1010
+
+
+# Short conv on the packed q|k|v columns (3 x 16 heads x 128 channels) at the 4 x 8192
+# prefill size, and its multi-step update at the 64 x 8 verify size.
+CONV_PREFILL = ConvCase("conv_prefill_4x8192_c6144_w4", [8192] * 4, 3 * 16 * 128, 4,
+                        pool_slots=4, seed=1010)
+CONV_UPDATE = ConvCase("conv_update_64x8_c6144_w4_pool256", [], 3 * 16 * 128, 4,
+                       pool_slots=256, batch=64, steps=8, seed=1011)
+
+
+def make_conv(case: ConvCase):
+    """x bf16 [T, C] ~ N(0, 1); weight bf16 [C, W] ~ N(0, 0.5^2); bias bf16 [C] ~ N(0, 0.1^2)
+    (or None); windows bf16 [slots, W-1, C] ~ N(0, 1); window indices: a seeded
+    permutation (prefill: one per sequence; update: one per row)."""
+    rng = np.random.default_rng(case.seed)
+    C, W = case.channels, case.width
+    update = case.batch > 0
+    T = case.batch * case.steps if update else int(sum(case.seq_lens))
+    x = _bf16(rng, (T, C))
+    weight = _bf16(rng, (C, W), std=0.5)
+    bias = _bf16(rng, (C,), std=0.1) if case.bias else None
+    state = _bf16(rng, (case.pool_slots, W - 1, C)) if case.pool_slots else None
+    rows = case.batch if update else len(case.seq_lens)
+    idx = None
+    if case.pool_slots:
+        perm = rng.permutation(max(case.pool_slots, rows))[:rows]
+        idx = torch.from_numpy(perm.astype(np.int32))
+    out = dict(x=x, weight=weight, bias=bias, state=state, state_idx=idx, width=W)
+    if update:
+        out["num_steps"] = case.steps
+    else:
+        lens = [int(v) for v in case.seq_lens]
+        out["cu_seqlens"] = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    return out
+
+
 def make_mixed(case: MixedCase):
     """Draw one mixed step: the prefill and spec workloads, the token order of the merged
     layer output (non_spec_idx [T_prefill], spec_idx [B*T], int32, disjoint), the output

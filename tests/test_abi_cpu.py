@@ -24,7 +24,8 @@ def test_exports_every_declared_symbol(lib):
     names = L.header_entry_points()
     assert set(names) >= {"kda_chunk_prefill", "kda_recurrent_verify", "kda_last_error",
                           "kda_abi_version", "kda_chunk_prefill_workspace_size",
-                          "kda_commit_accepted", "kda_gated_rmsnorm"}
+                          "kda_commit_accepted", "kda_gated_rmsnorm",
+                          "kda_causal_conv1d_prefill", "kda_causal_conv1d_update"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -193,3 +194,25 @@ def test_norm_accepts_interleaved_views(lib):
     d2.x_token_stride = d2.gate_token_stride = d2.y_token_stride = 2 * 2 * 128
     st = _norm(lib, d2, x=_fake(1), gate=ctypes.c_void_p(0x10000 + 100), y=_fake(1))
     assert st == INVALID
+
+
+def _cvdesc(N=2, T=16, steps=0, C=64, W=4, slots=4, silu=1):
+    return B.ConvDesc(N, T, steps, C, W, slots, silu, 0, 0)
+
+
+def test_conv_rejects_bad_arguments(lib):
+    f = _fake
+    pre = lambda d, y=None: lib.kda_causal_conv1d_prefill(f(1), f(2), None, f(3), f(4), None,
+                                                          y if y is not None else f(8),
+                                                          ctypes.byref(d), None)
+    upd = lambda d, inter=None: lib.kda_causal_conv1d_update(f(1), f(2), None, f(4), f(5),
+                                                             inter if inter is not None else f(9),
+                                                             f(12), ctypes.byref(d), None)
+    assert pre(_cvdesc(W=5)) == UNSUPPORTED
+    assert pre(_cvdesc(C=12)) == INVALID                  # not a multiple of 8
+    assert pre(_cvdesc(slots=1)) == INVALID               # fewer windows than sequences
+    assert pre(_cvdesc(), y=f(1)) == INVALID and b"overlap" in lib.kda_last_error()
+    assert upd(_cvdesc(N=2, T=16, steps=8)) not in (INVALID, UNSUPPORTED)   # passes checks
+    assert upd(_cvdesc(N=2, T=15, steps=8)) == INVALID    # total != B * T
+    assert upd(_cvdesc(N=2, T=16, steps=8), inter=f(4)) == INVALID   # windows overlap the pool
+    assert pre(_cvdesc(N=0, T=0)) == KDA_OK
