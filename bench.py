@@ -216,6 +216,9 @@ def summarize(prof_dirs, workload, out_md, mode_flag):
             store = json.load(f)
     except (OSError, ValueError):
         store = {}
+    # Entries of workloads this script no longer measures are dropped.
+    store = {k: v for k, v in store.items()
+             if k.rpartition("@")[2] in (MAIN_WORKLOAD, EXTRAS_WORKLOAD)}
     lines += ["| kernel | FETCH_SIZE KiB/dispatch (raw) | WRITE_SIZE KiB/dispatch (raw) | "
               "calibrated HBM MB/dispatch |", "|---|---|---|---|"]
     for key, cs in sorted(counters.items()):

@@ -456,7 +456,8 @@ void prefill_scan_kernel(PrefillParams p) {
     // Each chunk: copy chunk j+1 into LDS, pull chunk j+2 into L2 (the copies then hit
     // L2 instead of paying the full memory latency), wait for the copies only: vmcnt
     // counts in issue order, so NTOUCH outstanding operations left means exactly the
-    // touches are still in flight.
+    // touches are still in flight.  The previous chunk's output stores are issued after
+    // that wait, so their write acknowledgements stay off this chunk's critical path.
     using CC = ChunkCopy<NC, NB>;
     const bool copy_vt = has_vt && !wk.zero_v;
     const bool store = has_vt && wk.write_out;
@@ -472,18 +473,22 @@ void prefill_scan_kernel(PrefillParams p) {
       }
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      if (j + 1 < je)
-        CC(p, recbase, cs, ce, j + 1, h, v0, cw, copy_vt, lane, par ? lds0 : lds1, vt_off).all();
-      // Chunk j's scatter indices, read when its outputs are stored at the next chunk.
+      // Chunk j's scatter indices (read when its outputs are stored at the next chunk)
+      // go first, so the wait below covers them before the next barrier.
       if (wk.write_out && p.out_idx && cw == 0)
         copy_out_index(p, cs, ce, j, lane, lds_addr(sidx[par]));
-      if (j > jb && store)
-        store_out_tile<NB>(p, sout[par ^ 1][w], sidx[par ^ 1], cs, ce, j - 1, h, v0, lane);
       if (j + 1 < je) {
+        CC(p, recbase, cs, ce, j + 1, h, v0, cw, copy_vt, lane, par ? lds0 : lds1, vt_off).all();
         CC(p, recbase, cs, ce, min(j + 2, je - 1), h, v0, cw, copy_vt, lane, lds0, vt_off)
             .touch(lane, sink);
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CC::NTOUCH) : "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
+      // The previous chunk's output tile, after the wait: its stores complete while the
+      // compute waves work on chunk j, and only the next chunk's wait can include them.
+      if (j > jb && store)
+        store_out_tile<NB>(p, sout[par ^ 1][w], sidx[par ^ 1], cs, ce, j - 1, h, v0, lane);
     }
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
