@@ -253,6 +253,41 @@ def roofline(bytes_, flops, seconds, bound="hbm"):
             "frac": round(ach / MFMA_BF16_PEAK_TFS, 4), "traffic": None}
 
 
+def measured_ceilings():
+    """Ceilings measured on this GPU in the same run, beside the published peaks: a
+    write-only fill and an elementwise copy through the shader (1 GiB each way), and a
+    dense bf16 GEMM from the vendor library (8192 x 8192 x 8192, contiguous operands)."""
+    def timed(fn, iters):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / iters
+
+    a = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    t_fill = timed(lambda: b.fill_(2.0), 20)
+    t_copy = timed(lambda: torch.mul(a, 1.0, out=b), 20)
+    del a, b
+    m = 8192
+    x = torch.randn(m, m, device="cuda").to(torch.bfloat16)
+    y = torch.randn(m, m, device="cuda").to(torch.bfloat16)
+    z = torch.empty(m, m, dtype=torch.bfloat16, device="cuda")
+    t_gemm = timed(lambda: torch.matmul(x, y, out=z), 10)
+    del x, y, z
+    torch.cuda.empty_cache()
+    return {"write_only_GBs": round(CALIB_BYTES / t_fill / 1e9, 1),
+            "copy_GBs": round(2 * CALIB_BYTES / t_copy / 1e9, 1),
+            "gemm_bf16_TFs": round(2 * m ** 3 / t_gemm / 1e12, 1),
+            "how": "fill_ of 1 GiB; x*1.0 over 1 GiB (read + write); torch.matmul bf16 8192^3"}
+
+
 def calibration_copies():
     """An elementwise kernel that reads 1 GiB and writes 1 GiB (a copy through the shader,
     unlike copy_, which may use the DMA engine and escape the counters)."""
@@ -534,6 +569,16 @@ def main():
     rl = dict(kernels[dom][1])
     rl["kernel"] = dom
 
+    log("measured ceilings (fill, copy, GEMM)")
+    ceil = measured_ceilings()
+    rl_p_hbm = roofline(prefill_bytes, 0, s_prefill)
+    rl_p_mfma = roofline(0, prefill_flops, s_prefill, bound="mfma")
+    vs_measured = {
+        "verify_vs_write_only": round(kernels["kda_verify"][1]["achieved"] / ceil["write_only_GBs"], 4),
+        "prefill_hbm_vs_copy": round(rl_p_hbm["achieved"] / ceil["copy_GBs"], 4),
+        "prefill_mfma_vs_gemm": round(rl_p_mfma["achieved"] / ceil["gemm_bf16_TFs"], 4),
+    }
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"oracle baseline on {args.cpu_tokens} tokens/sequence")
@@ -577,11 +622,13 @@ def main():
         "roofline": rl,
         "roofline_by_kernel": {k: v[1] for k, v in kernels.items()},
         "roofline_prefill_call": {
-            "hbm": roofline(prefill_bytes, 0, s_prefill),
-            "mfma": roofline(0, prefill_flops, s_prefill, bound="mfma"),
+            "hbm": rl_p_hbm,
+            "mfma": rl_p_mfma,
             "roofline_frac": round(max(prefill_bytes / (HBM_PEAK_GBS * 1e9),
                                        prefill_flops / (MFMA_BF16_PEAK_TFS * 1e12)) / s_prefill, 4),
         },
+        "measured_ceilings": ceil,
+        "fraction_of_measured": vs_measured,
         "cpu_baseline": cpu,
         "next_rows": extras,
         "context": {"flashkda_gb300_us_per_layer_8192x4": 146,
