@@ -143,6 +143,10 @@ EXTRAS_WORKLOAD = (f"commit after {W.VERIFY.name} + conv {W.CONV_PREFILL.name} /
                    f"{W.SINGLE_LONG.name} + mixed step {W.MIXED.name}")
 
 
+N_XCD = 8           # MI355X: XCDs (GRBM_GUI_ACTIVE is read once per XCD)
+N_SIMD = 256 * 4    # compute units x SIMDs
+
+
 def targs(kernel_name):
     """Template arguments of a (demangled) kernel name, e.g. '<4, 4, 1, 1>' (or '')."""
     m = re.search(r"_kernel(<[^()]*>)\(", kernel_name)
@@ -192,8 +196,15 @@ def summarize(prof_dirs, workload, out_md, mode_flag):
              "    rocprofv3 --pmc WRITE_SIZE --kernel-trace --output-format csv -d OUT/prof_write "
              f"-o write -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline {mode_flag} "
              "--calib-copy",
+             "    rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_INSTS_VALU_MFMA_MOPS_BF16 "
+             "SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --kernel-trace "
+             "--output-format csv -d OUT/prof_mfma -o mfma -- python3 $R/bench.py --steps 3 "
+             f"--warmup 1 --no-cpu-baseline {mode_flag}   (main mode only)",
+             "    rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE --kernel-trace "
+             "--output-format csv -d OUT/prof_lds -o lds -- python3 $R/bench.py --steps 3 "
+             f"--warmup 1 --no-cpu-baseline {mode_flag}   (main mode only)",
              "    python3 $R/bench.py --summarize OUT/prof_trace OUT/prof_fetch OUT/prof_write "
-             f"{mode_flag} --summary-out <this file>", "",
+             f"[OUT/prof_mfma OUT/prof_lds] {mode_flag} --summary-out <this file>", "",
              "Kernel durations (kernel-trace run only):", "",
              "| kernel | dispatches | avg us | min us | max us |", "|---|---|---|---|---|"]
     def label(key, keys):
@@ -235,6 +246,36 @@ def summarize(prof_dirs, workload, out_md, mode_flag):
             store[f"{k}@{workload}"] = {"fetch_bytes": fb, "write_bytes": wb,
                                        "source_hash": source_hash(key[0]),
                                        "calibration": factors}
+    # MFMA and LDS counters (extra --pmc passes, when given): executed MFMA operations
+    # (the MOPS counters count operations / 512 per data type), MFMA busy share of
+    # all SIMD cycles (GRBM_GUI_ACTIVE: the GPU's busy clock, summed here over the
+    # XCDs), LDS bank-conflict cycles against LDS-busy cycles.
+    mf_rows = []
+    for key, cs in sorted(counters.items()):
+        mops = [cs.get(c) for c in ("SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                                    "SQ_INSTS_VALU_MFMA_MOPS_F32")]
+        if all(m is None for m in mops) and "SQ_LDS_BANK_CONFLICT" not in cs:
+            continue
+        avg = lambda c: (sum(cs[c]) / len(cs[c])) if cs.get(c) else None
+        row = [label(key, counters)]
+        if any(m is not None for m in mops):
+            f16, b16, f32 = (avg(c) or 0.0 for c in ("SQ_INSTS_VALU_MFMA_MOPS_F16",
+                                                      "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                                                      "SQ_INSTS_VALU_MFMA_MOPS_F32"))
+            row.append(f"{(f16 + b16 + f32) * 512 / 1e9:.2f} (f16 {f16 * 512 / 1e9:.2f}, "
+                       f"bf16 {b16 * 512 / 1e9:.2f}, f32 {f32 * 512 / 1e9:.2f})")
+            busy, act = avg("SQ_VALU_MFMA_BUSY_CYCLES"), avg("GRBM_GUI_ACTIVE")
+            row.append(f"{100 * busy / (act / N_XCD * N_SIMD):.1f}" if busy and act else "-")
+        else:
+            row += ["-", "-"]
+        conf, lact = avg("SQ_LDS_BANK_CONFLICT"), avg("SQ_LDS_IDX_ACTIVE")
+        row.append(f"{100 * conf / lact:.1f}" if conf is not None and lact else "-")
+        mf_rows.append("| " + " | ".join(row) + " |")
+    if mf_rows:
+        lines += ["", "MFMA and LDS counters (each from its own --pmc pass; MFMA operations "
+                  "= MOPS counters x 512):", "",
+                  "| kernel | MFMA operations per dispatch (1e9) | MFMA busy % of SIMD cycles "
+                  "| LDS bank-conflict % of LDS-active cycles |", "|---|---|---|---|"] + mf_rows
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
     os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
