@@ -66,6 +66,7 @@ def cpu_baseline(case, tokens_per_seq):
     from oracle import kda_oracle as O
     data = W.make_prefill(case)
     cu = data["cu_seqlens"].numpy().astype(np.int64)
+    tokens_per_seq = min(tokens_per_seq, int(np.min(np.diff(cu))))
     rows = np.concatenate([np.arange(cu[n], cu[n] + tokens_per_seq) for n in range(len(cu) - 1)])
     f = W.to_f64
     sub_cu = np.arange(0, len(rows) + 1, tokens_per_seq)
@@ -480,8 +481,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=2048,
-                    help="tokens per sequence in the oracle's timed sample")
+    ap.add_argument("--cpu-tokens", type=int, default=8192,
+                    help="tokens per sequence in the oracle's timed sample (8192: the whole "
+                         "4 x 8192 workload, about 10 s of one host core)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run 1 GiB device copies (counter calibration under rocprofv3)")
     ap.add_argument("--summarize", nargs="+", metavar="PROF_DIR",
