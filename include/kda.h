@@ -249,6 +249,7 @@ typedef struct kda_conv_desc {
  *               one after its last token (kept when the sequence is empty).  Two
  *               sequences must not name one window.
  *   y           bf16 [T_total, C], token-strided; must not overlap x or conv_state
+ * (T_total / 16 + N) * ceil(C / 2048) above 2^24 - 1 returns KDA_ERR_UNSUPPORTED.
  */
 kda_status kda_causal_conv1d_prefill(const void* x, const void* weight, const void* bias,
                                      const int32_t* cu_seqlens, void* conv_state,

@@ -378,6 +378,10 @@ kda_status kda_causal_conv1d_prefill(const void* x, const void* weight, const vo
       return fail(KDA_ERR_INVALID_ARGUMENT, "y overlaps conv_state");
   }
   if (N == 0) return ok();
+  // One 256-thread workgroup per (16-token row slot, 2048-channel block), in a 1-D grid.
+  if (kda::conv_prefill_workgroups(N, T, desc->channels) > (int64_t{1} << 24) - 1)
+    return fail(KDA_ERR_UNSUPPORTED, "conv prefill of %d tokens x %d channels: too many workgroups",
+                T, desc->channels);
   p.cu = cu_seqlens;
   p.state = desc->width > 1 ? static_cast<uint16_t*>(conv_state) : nullptr;
   p.state_idx = state_idx;

@@ -16,7 +16,8 @@ namespace {
 
 constexpr int CONV_THREADS = 256;
 constexpr int CONV_CPT = 8;                                 // channels per thread
-constexpr int CONV_CPB = CONV_THREADS * CONV_CPT;           // channels per workgroup
+static_assert(CONV_CPB == CONV_THREADS * CONV_CPT, "channels per workgroup");
+static_assert(CONV_ROWS >= 3, "a row slot after the first reads its W - 1 <= 3 history rows from x");
 constexpr int CONV_BATCH = 16;                              // token rows loaded at once
 
 __device__ __forceinline__ void unpack8(uint4 w, float* f) {
@@ -87,24 +88,29 @@ __device__ __forceinline__ void push_hist(uint4 (&hist)[3], uint4 x) {
 
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
-// Prefill outputs: one workgroup per (64-token chunk slot, channel block).
+// Prefill outputs: one short-lived workgroup per (16-token row slot, channel block),
+// channel blocks fastest in a 1-D grid, so the workgroups running at any moment read
+// and write whole token rows; the W-1 history rows before a slot are re-read (mostly
+// from L2).  On MI355X at 4 x 8192 tokens x 6144 channels this runs at 160 us against
+// 188 us for 64-token slots with the slots fastest.
 template <int W>
 __global__ __launch_bounds__(CONV_THREADS) void conv_prefill_kernel(ConvParams p) {
-  const int slot = blockIdx.x;
-  const int c0 = blockIdx.y * CONV_CPB + threadIdx.x * CONV_CPT;
-  // Chunk map: sequence n owns slots [cu[n]/64 + n, ...); the last n whose first slot is
-  // <= this one (binary search on the device, no host sync).
+  const int cblocks = (p.C + CONV_CPB - 1) / CONV_CPB;
+  const int slot = blockIdx.x / cblocks;
+  const int c0 = (blockIdx.x % cblocks) * CONV_CPB + threadIdx.x * CONV_CPT;
+  // Row-slot map: sequence n owns slots [cu[n]/16 + n, ...); the last n whose first slot
+  // is <= this one (binary search on the device, no host sync).
   int lo = 0, hi = p.N - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (p.cu[mid] / CHUNK + mid <= slot) lo = mid; else hi = mid - 1;
+    if (p.cu[mid] / CONV_ROWS + mid <= slot) lo = mid; else hi = mid - 1;
   }
   const int n = lo;
   const int cs = p.cu[n], ce = p.cu[n + 1];
-  const int jc = slot - (cs / CHUNK + n);
-  if (jc * CHUNK >= ce - cs || c0 >= p.C) return;
-  const int t0 = cs + jc * CHUNK;
-  const int L = min(CHUNK, ce - t0);
+  const int jc = slot - (cs / CONV_ROWS + n);
+  if (jc * CONV_ROWS >= ce - cs || c0 >= p.C) return;
+  const int t0 = cs + jc * CONV_ROWS;
+  const int L = min(CONV_ROWS, ce - t0);
   ConvTaps k;
   load_taps<W>(p, c0, k);
   // History: the W-1 inputs before t0 (slots 3 - (W-1) .. 2 of hist; the rest zero).
@@ -224,7 +230,7 @@ template <int W>
 hipError_t conv_prefill_w(const ConvParams& p, hipStream_t s) {
   const unsigned cblocks = static_cast<unsigned>((p.C + CONV_CPB - 1) / CONV_CPB);
   if (p.T_total > 0) {
-    const dim3 grid(static_cast<unsigned>(chunk_slots(p.N, p.T_total)), cblocks);
+    const dim3 grid(static_cast<unsigned>(conv_prefill_workgroups(p.N, p.T_total, p.C)));
     hipLaunchKernelGGL(conv_prefill_kernel<W>, grid, dim3(CONV_THREADS), 0, s, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -72,6 +72,14 @@ struct NormParams {
   int64_t x_st, g_st, y_st;
 };
 
+// Conv prefill work split: one workgroup per (CONV_ROWS-token row slot, CONV_CPB-channel
+// block); sequence n owns row slots from cu[n] / CONV_ROWS + n on.
+constexpr int CONV_ROWS = 16;
+constexpr int CONV_CPB = 2048;
+inline int64_t conv_prefill_workgroups(int N, int T_total, int C) {
+  return (static_cast<int64_t>(T_total) / CONV_ROWS + N) * ((C + CONV_CPB - 1) / CONV_CPB);
+}
+
 struct ConvParams {
   const uint16_t* x;
   const uint16_t* weight;    // [C, W] bf16

@@ -216,3 +216,18 @@ def test_conv_rejects_bad_arguments(lib):
     assert upd(_cvdesc(N=2, T=15, steps=8)) == INVALID    # total != B * T
     assert upd(_cvdesc(N=2, T=16, steps=8), inter=f(4)) == INVALID   # windows overlap the pool
     assert pre(_cvdesc(N=0, T=0)) == KDA_OK
+
+
+def test_conv_prefill_launch_size_limit(lib):
+    # One workgroup per (16-token row slot, 2048-channel block) in a 1-D grid: more than
+    # 2^24 - 1 workgroups is refused on the host.  x and y sit far apart so that only the
+    # size check can object.
+    def pre(T, C):
+        d = _cvdesc(N=1, T=T, C=C, slots=0)
+        return lib.kda_causal_conv1d_prefill(ctypes.c_void_p(1 << 46), _fake(2), None, _fake(3),
+                                             None, None, ctypes.c_void_p(1 << 47),
+                                             ctypes.byref(d), None)
+    assert pre(2**31 - 1, 6144) == UNSUPPORTED and b"workgroups" in lib.kda_last_error()
+    limit_T = 16 * ((2**24 - 1) // 3 - 1)                  # (T/16 + 1) * 3 <= 2^24 - 1
+    assert pre(limit_T, 6144) not in (INVALID, UNSUPPORTED)
+    assert pre(limit_T + 16 * 2, 6144) == UNSUPPORTED
