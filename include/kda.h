@@ -218,6 +218,7 @@ typedef struct kda_norm_desc {
  *   y               bf16 [tokens, H, 128]; may be x itself (same pointer and stride),
  *                   must not overlap gate
  *   rstd            fp32 [tokens, H] or NULL (not written)
+ * tokens * H above 32 * (2^24 - 1) rows returns KDA_ERR_UNSUPPORTED.
  */
 kda_status kda_gated_rmsnorm(const void* x, const void* gate, const float* weight, void* y,
                              float* rstd, const kda_norm_desc* desc, void* stream);

@@ -460,10 +460,8 @@ kda_status kda_gated_rmsnorm(const void* x, const void* gate, const float* weigh
     return fail(KDA_ERR_INVALID_ARGUMENT, "y overlaps x (only y == x with equal strides is allowed)");
   if (rstd && overlaps(span_of(rstd, static_cast<int64_t>(T) * H, 1, 1, 4), sy))
     return fail(KDA_ERR_INVALID_ARGUMENT, "rstd overlaps y");
-  int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return fail(KDA_ERR_HIP, "device query failed: %s", hipGetErrorString(e));
+  if (kda::norm_workgroups(static_cast<int64_t>(T) * H) > (int64_t{1} << 24) - 1)
+    return fail(KDA_ERR_UNSUPPORTED, "norm over %d x %d rows: too many workgroups", T, H);
   kda::NormParams p{};
   p.x = static_cast<const uint16_t*>(x);
   p.gate = static_cast<const uint16_t*>(gate);
@@ -474,7 +472,7 @@ kda_status kda_gated_rmsnorm(const void* x, const void* gate, const float* weigh
   p.tokens = T;
   p.H = H;
   p.x_st = xs; p.g_st = gs; p.y_st = ys;
-  e = kda::launch_gated_rmsnorm(p, cus, static_cast<hipStream_t>(stream));
+  const hipError_t e = kda::launch_gated_rmsnorm(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "norm launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -142,7 +142,10 @@ inline int64_t chunk_slots(int N, int T_total) { return static_cast<int64_t>(T_t
 // Launchers (enqueue only; return the hipGetLastError() of the launch).
 hipError_t launch_verify(const VerifyParams& p, hipStream_t s);
 hipError_t launch_commit(const CommitParams& p, hipStream_t s);
-hipError_t launch_gated_rmsnorm(const NormParams& p, int cus, hipStream_t s);
+// Gated RMSNorm: one short-lived workgroup per NORM_ROWS_PER_WG rows.
+constexpr int NORM_ROWS_PER_WG = 32;
+inline int64_t norm_workgroups(int64_t rows) { return (rows + NORM_ROWS_PER_WG - 1) / NORM_ROWS_PER_WG; }
+hipError_t launch_gated_rmsnorm(const NormParams& p, hipStream_t s);
 hipError_t launch_conv_prefill(const ConvParams& p, hipStream_t s);
 hipError_t launch_conv_update(const ConvParams& p, hipStream_t s);
 // Prefill phases: bit 0 = intra-chunk kernel, bit 1 = state-scan kernel.

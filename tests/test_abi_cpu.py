@@ -182,9 +182,19 @@ def test_norm_rejects_bad_arguments(lib):
     assert _norm(lib, _ndesc(T=0)) == KDA_OK
 
 
+def test_norm_launch_size_limit(lib):
+    # One short-lived workgroup per 32 rows: more than 2^24 - 1 workgroups is refused.
+    far = lambda k: ctypes.c_void_p(k << 44)
+    over = _ndesc(T=2**31 - 1, H=1)
+    assert _norm(lib, over, x=far(1), gate=far(2), y=far(3)) == UNSUPPORTED
+    assert b"workgroups" in lib.kda_last_error()
+    at = _ndesc(T=32 * (2**24 - 1) // 16, H=16)              # exactly 2^24 - 1 workgroups
+    assert _norm(lib, at, x=far(1), gate=far(2), y=far(3)) not in (INVALID, UNSUPPORTED)
+
+
 def test_norm_accepts_interleaved_views(lib):
     # x and gate interleaved rows of one fused buffer (stride 3*H*128), y in place over x:
-    # validation passes (without a GPU the call then fails at the device query).
+    # validation passes (without a GPU the call then fails at the launch).
     d = _ndesc(T=4, H=2)
     d.x_token_stride = d.gate_token_stride = d.y_token_stride = 3 * 2 * 128
     st = _norm(lib, d, x=_fake(1), gate=ctypes.c_void_p(0x10000 + 2 * 128 * 2), y=_fake(1))
