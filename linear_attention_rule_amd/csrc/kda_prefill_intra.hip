@@ -56,6 +56,14 @@ __device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t& hi, uin
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Record stores are non-temporal: the 61 KiB records of a call outgrow the caches, and the
+// scan that reads them back ran 3-4% faster when they did not pass through as ordinary
+// writes (4 x 8192 x 16 heads on MI355X: scan 266-271 us -> 255-260 us).
+template <class T16>
+__device__ __forceinline__ void rec_store(unsigned char* dst, const T16& v) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(dst));
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // Workgroup barrier for LDS hand-offs only: waits for this wave's LDS operations, not
@@ -243,7 +251,7 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
     }
   }
   lds_barrier();
-  if (tid < 128) reinterpret_cast<float*>(rec + REC_GAMMA_OFF)[tid] = sm.Eb[4][tid];
+  if (tid < 128) __builtin_nontemporal_store(sm.Eb[4][tid], reinterpret_cast<float*>(rec + REC_GAMMA_OFF) + tid);
 
   // ---- operands.  b = la (in-block cumulative), Lf = 2^b <= 1, Rf = 2^-b >= 1.
   bf16x8 KL[4], QLh[4], QLl[4], Rh[4], Rl[4];
@@ -299,8 +307,8 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
       QLl[s] = as_bf16x8(qlp);
       Rh[s] = as_bf16x8(rhp);
       Rl[s] = as_bf16x8(rlp);
-      *reinterpret_cast<half8*>(rec + (FR_KG + 4 * w + s) * 1024 + lane * 16) = kg;
-      *reinterpret_cast<half8*>(rec + (FR_QG + 4 * w + s) * 1024 + lane * 16) = qg;
+      rec_store(rec + (FR_KG + 4 * w + s) * 1024 + lane * 16, kg);
+      rec_store(rec + (FR_QG + 4 * w + s) * 1024 + lane * 16, qg);
     }
   }
   if (w < 3) {
@@ -449,14 +457,14 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
                   static_cast<_Float16>(ta.z * ba.z), static_cast<_Float16>(ta.w * ba.w),
                   static_cast<_Float16>(tb.x * bb.x), static_cast<_Float16>(tb.y * bb.y),
                   static_cast<_Float16>(tb.z * bb.z), static_cast<_Float16>(tb.w * bb.w)};
-      *reinterpret_cast<half8*>(rec + (FR_TP + fi) * 1024 + lane * 16) = tf;
+      rec_store(rec + (FR_TP + fi) * 1024 + lane * 16, tf);
       const float4 pa = *reinterpret_cast<const float4*>(sm.P + row * ATS + c0);
       const float4 pb = *reinterpret_cast<const float4*>(sm.P + row * ATS + c1);
       half8 pf = {static_cast<_Float16>(pa.x), static_cast<_Float16>(pa.y),
                   static_cast<_Float16>(pa.z), static_cast<_Float16>(pa.w),
                   static_cast<_Float16>(pb.x), static_cast<_Float16>(pb.y),
                   static_cast<_Float16>(pb.z), static_cast<_Float16>(pb.w)};
-      *reinterpret_cast<half8*>(rec + (FR_PM + fi) * 1024 + lane * 16) = pf;
+      rec_store(rec + (FR_PM + fi) * 1024 + lane * 16, pf);
     }
     // K_C^T fragments (channel block cb, token k-step s'): lane (r, g) holds channel
     // 16cb + r, tokens kperm(s', g, 0..7).
@@ -468,8 +476,7 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
         const _Float16* src = sm.u.late.KCt + (16 * cb + m) * KCS;
         const uint2 a = *reinterpret_cast<const uint2*>(src + kperm(sp, g, 0));
         const uint2 b = *reinterpret_cast<const uint2*>(src + kperm(sp, g, 4));
-        *reinterpret_cast<uint4*>(rec + (FR_KC + 2 * cb + sp) * 1024 + lane * 16) =
-            make_uint4(a.x, a.y, b.x, b.y);
+        rec_store(rec + (FR_KC + 2 * cb + sp) * 1024 + lane * 16, make_uint4(a.x, a.y, b.x, b.y));
       }
     }
   }
