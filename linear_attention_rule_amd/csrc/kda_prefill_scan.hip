@@ -454,11 +454,15 @@ void prefill_scan_kernel(PrefillParams p) {
 
   if (copier) {
     // Each chunk: copy chunk j+1 into LDS, pull chunk j+2 into L2 (the copies then hit
-    // L2 instead of paying the full memory latency), wait for the copies only: vmcnt
-    // counts in issue order, so NTOUCH outstanding operations left means exactly the
+    // L2 instead of paying the full memory latency; see TOUCH), wait for the copies only:
+    // vmcnt counts in issue order, so NTOUCH outstanding operations left means exactly the
     // touches are still in flight.  The previous chunk's output stores are issued after
     // that wait, so their write acknowledgements stay off this chunk's critical path.
     using CC = ChunkCopy<NC, NB>;
+    // The touch-ahead pays off with four workgroups per pair (two compute waves each:
+    // 4 x 8192 x 16 heads, 258 -> 253 us) and costs with two (four compute waves: 8 x 2048
+    // x 16 heads, 91 -> 96 us), so only the former issues it.
+    constexpr bool TOUCH = (NW == 2);
     const bool copy_vt = has_vt && !wk.zero_v;
     const bool store = has_vt && wk.write_out;
     const uint32_t lds0 = lds_addr(srec0), lds1 = lds_addr(srec1);
@@ -467,9 +471,13 @@ void prefill_scan_kernel(PrefillParams p) {
       const int par = (j - jb) & 1;
       if (j == jb) {
         CC(p, recbase, cs, ce, jb, h, v0, cw, copy_vt, lane, lds0, vt_off).all();
-        CC(p, recbase, cs, ce, min(jb + 1, je - 1), h, v0, cw, copy_vt, lane, lds1, vt_off)
-            .touch(lane, sink);
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CC::NTOUCH) : "memory");
+        if (TOUCH) {
+          CC(p, recbase, cs, ce, min(jb + 1, je - 1), h, v0, cw, copy_vt, lane, lds1, vt_off)
+              .touch(lane, sink);
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CC::NTOUCH) : "memory");
+        } else {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
       }
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
@@ -479,9 +487,13 @@ void prefill_scan_kernel(PrefillParams p) {
         copy_out_index(p, cs, ce, j, lane, lds_addr(sidx[par]));
       if (j + 1 < je) {
         CC(p, recbase, cs, ce, j + 1, h, v0, cw, copy_vt, lane, par ? lds0 : lds1, vt_off).all();
-        CC(p, recbase, cs, ce, min(j + 2, je - 1), h, v0, cw, copy_vt, lane, lds0, vt_off)
-            .touch(lane, sink);
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CC::NTOUCH) : "memory");
+        if (TOUCH) {
+          CC(p, recbase, cs, ce, min(j + 2, je - 1), h, v0, cw, copy_vt, lane, lds0, vt_off)
+              .touch(lane, sink);
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CC::NTOUCH) : "memory");
+        } else {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
       } else {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
