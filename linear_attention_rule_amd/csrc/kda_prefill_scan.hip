@@ -582,11 +582,15 @@ void prefill_scan_kernel(PrefillParams p) {
 }
 
 // Segment start states: S_in(1) comes from segment 0; then, for each middle segment s in
-// order, S_in(s+1) = M_s S_in(s) + B_s in fp32.  One workgroup per (sequence, head,
-// 32-column slice); thread t computes rows 4(t/8) .. +3 and columns 4(t%8) .. +3 of the
-// slice, reading rows of M_s from global memory and the slice of S_in(s) from LDS.
+// order, S_in(s+1) = M_s S_in(s) + B_s in fp32.  One workgroup of 1024 threads per
+// (sequence, head, 32-column slice); thread t computes row t/8 and columns 4(t%8) .. +3 of
+// the slice, reading its row of M_s from global memory (L2: the four slices of a pair
+// share it) and the slice of S_in(s) from LDS.  The few workgroups leave most CUs idle,
+// so 16 waves each hide the load latency (1 x 16384 x 16 heads: 26 -> 15 us against 256
+// threads with 4 rows each).
 constexpr int COMB_COLS = 32;
-__global__ __launch_bounds__(256) void seg_combine_kernel(PrefillParams p) {
+constexpr int COMB_THREADS = 1024;
+__global__ __launch_bounds__(COMB_THREADS) void seg_combine_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) float sin_s[D][COMB_COLS];
   const int G = p.seg_G;
   const int slices = D / COMB_COLS;
@@ -594,7 +598,7 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(PrefillParams p) {
   const int c0 = (blockIdx.x % slices) * COMB_COLS;
   const int n = pair / p.H, h = pair % p.H;
   const int tid = threadIdx.x;
-  const int r0 = 4 * (tid >> 3);            // rows r0 .. r0 + 3
+  const int r = tid >> 3;                   // row r
   const int cq = 4 * (tid & 7);             // columns cq .. cq + 3 of the slice
   for (int s = 1; s <= G - 2; ++s) {
     const float* sin = seg_slot(p, n, h, s - 1);
@@ -602,39 +606,27 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(PrefillParams p) {
     const float* B = seg_slot(p, n, h, seg_b_slot(G, s));
     float* sout = seg_slot(p, n, h, s);
     __syncthreads();   // the previous step's reads of sin_s are done
-    for (int e = tid; e < D * COMB_COLS / 4; e += 256) {
-      const int r = e / (COMB_COLS / 4), c = 4 * (e % (COMB_COLS / 4));
-      *reinterpret_cast<float4*>(&sin_s[r][c]) =
-          *reinterpret_cast<const float4*>(sin + r * D + c0 + c);
+    for (int e = tid; e < D * COMB_COLS / 4; e += COMB_THREADS) {
+      const int rr = e / (COMB_COLS / 4), c = 4 * (e % (COMB_COLS / 4));
+      *reinterpret_cast<float4*>(&sin_s[rr][c]) =
+          *reinterpret_cast<const float4*>(sin + rr * D + c0 + c);
     }
     __syncthreads();
-    float acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float4 b4 = *reinterpret_cast<const float4*>(B + (r0 + i) * D + c0 + cq);
-      acc[i][0] = b4.x; acc[i][1] = b4.y; acc[i][2] = b4.z; acc[i][3] = b4.w;
-    }
+    const float4 b4 = *reinterpret_cast<const float4*>(B + r * D + c0 + cq);
+    float acc[4] = {b4.x, b4.y, b4.z, b4.w};
     for (int k = 0; k < D; k += 4) {
-      float4 m4[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) m4[i] = *reinterpret_cast<const float4*>(M + (r0 + i) * D + k);
+      const float4 m4 = *reinterpret_cast<const float4*>(M + r * D + k);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const float4 x = *reinterpret_cast<const float4*>(&sin_s[k + kk][cq]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float m = (kk == 0) ? m4[i].x : (kk == 1) ? m4[i].y : (kk == 2) ? m4[i].z : m4[i].w;
-          acc[i][0] += m * x.x;
-          acc[i][1] += m * x.y;
-          acc[i][2] += m * x.z;
-          acc[i][3] += m * x.w;
-        }
+        const float m = (kk == 0) ? m4.x : (kk == 1) ? m4.y : (kk == 2) ? m4.z : m4.w;
+        acc[0] += m * x.x;
+        acc[1] += m * x.y;
+        acc[2] += m * x.z;
+        acc[3] += m * x.w;
       }
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<float4*>(sout + (r0 + i) * D + c0 + cq) =
-          make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+    *reinterpret_cast<float4*>(sout + r * D + c0 + cq) = make_float4(acc[0], acc[1], acc[2], acc[3]);
     // The next step reads this slice of S_in(s+1) back after the barrier at its top.
   }
 }
@@ -688,7 +680,7 @@ hipError_t launch_prefill(const PrefillParams& p_in, int phases, hipStream_t s) 
     // combine; phase C: the later segments from their start states).
     if ((e = launch_scan<4, 4, SCAN_NB, MODE_SEG_A>(p, s)) != hipSuccess) return e;
     hipLaunchKernelGGL(seg_combine_kernel, dim3(static_cast<unsigned>(pairs * (D / COMB_COLS))),
-                       dim3(256), 0, s, p);
+                       dim3(COMB_THREADS), 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return launch_scan<2, 2, SCAN_NB, MODE_SEG_C>(p, s);
   }
