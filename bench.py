@@ -354,6 +354,52 @@ def time_calls(fn, iters, warmup=3):
     return e0.elapsed_time(e1) * 1e-3 / iters
 
 
+def verify_latency_b1(iters):
+    """The verify latency case (one row of 8 draft tokens at 16 heads): microseconds per
+    call with plain launches, and per call replayed from a HIP graph of 20 calls (launch
+    overhead excluded). Each of three replays is checked against a plain call first."""
+    case = W.VERIFY_B1
+    vd = to_dev(W.make_verify(case))
+    B, Tv, H = case.batch, case.steps, case.heads
+    out = torch.empty((B * Tv, H, D), dtype=torch.bfloat16, device="cuda")
+    inter = torch.empty((B, Tv, H, D, D), dtype=torch.float32, device="cuda")
+
+    def call():
+        recurrent_verify(vd["q"], vd["k"], vd["v"], vd["g"], vd["beta_logits"], vd["A_log"],
+                         vd["dt_bias"], vd["lower_bound"], vd["state_pool"], vd["state_idx"], Tv,
+                         intermediate=inter, out=out, scale=vd["scale"])
+
+    res = {"workload": case.name, "us_plain_launch": round(time_calls(call, 10 * iters) * 1e6, 2)}
+    call()
+    torch.cuda.synchronize()
+    ref = (out.clone(), inter.clone())
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            call()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(20):
+                call()
+        same = True
+        for _ in range(3):
+            out.zero_()
+            inter.zero_()
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            same = same and torch.equal(out, ref[0]) and torch.equal(inter, ref[1])
+        res["us_graph_replay"] = round(time_calls(graph.replay, iters) / 20 * 1e6, 2) if same else None
+        res["graph_replays_match_plain_call"] = bool(same)
+    except RuntimeError as e:
+        res["us_graph_replay"] = None
+        res["graph_error"] = str(e)[:200]
+    return res
+
+
 def bench_next_rows(iters):
     """The rows after the hot path: the rollback commit at the verify size, and one mixed
     speculative step (prefill segment and spec rows scattered into one layer output)."""
@@ -622,6 +668,9 @@ def main():
         "prefill_mfma_vs_gemm": round(rl_p_mfma["achieved"] / ceil["gemm_bf16_TFs"], 4),
     }
 
+    log("verify latency case (B = 1)")
+    lat_b1 = verify_latency_b1(args.steps)
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"oracle baseline on {args.cpu_tokens} tokens/sequence")
@@ -660,6 +709,7 @@ def main():
         "kernel_us": {"kda_prefill_intra": round(s_intra * 1e6, 2),
                       "kda_prefill_scan": round(s_scan * 1e6, 2),
                       "kda_verify": round(s_ver * 1e6, 2)},
+        "verify_latency_b1": lat_b1,
         "cold_cache_us": {"prefill": round(float(np.median(cold_p)) * 1e6, 2),
                           "verify": round(float(np.median(cold_v)) * 1e6, 2)},
         "roofline": rl,
