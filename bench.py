@@ -80,8 +80,14 @@ def cpu_baseline(case, tokens_per_seq):
     r1 = resource.getrusage(resource.RUSAGE_SELF)
     cpu = (r1.ru_utime - r0.ru_utime) + (r1.ru_stime - r0.ru_stime)
     tokens = len(rows)
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": tokens / wall, "unit": "tokens/s", "cores": max(1, round(cpu / wall)),
-            "kind": "oracle",
+            "kind": "oracle", "wall_s": round(wall, 2), "cpu_model": model,
             "sample": f"{case.name}: all {len(cu) - 1} sequences x {case.heads} heads, first "
                       f"{tokens_per_seq} tokens of each ({tokens} tokens, {wall:.1f} s wall, "
                       f"fp64 numpy token loop, {os.cpu_count()} host CPUs visible)"}
