@@ -553,8 +553,9 @@ def main():
                   "--extras-only" if extras else "--no-extras")
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for {args.gpus}); this build has no "
-              "multi-GPU path", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); the library runs the "
+              "path on one GPU (heads, sequences and verify rows shard without communication)",
+              file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
