@@ -49,7 +49,9 @@ outside [0, slots) marks a padding row whose outputs are zero and whose
 states are not written; in prefill, a start-state index outside the pool
 starts that sequence from the zero state.
 
-Parity pins for every function here live in ``tests/test_oracle_pins.py``.
+Parity pins for every function here live in ``tests/test_oracle_pins.py`` (recurrence,
+prefill, verify), ``tests/test_oracle_mixed_pins.py`` (scatter, commit),
+``tests/test_oracle_norm_pins.py`` and ``tests/test_oracle_conv_pins.py``.
 """
 
 from __future__ import annotations
