@@ -196,14 +196,13 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
       gg[2] = bf16lo_to_f32(gr[j].y); gg[3] = bf16hi_to_f32(gr[j].y);
       dt[4 * j] = dr[j].x; dt[4 * j + 1] = dr[j].y; dt[4 * j + 2] = dr[j].z; dt[4 * j + 3] = dr[j].w;
     }
-    const float eA = __builtin_amdgcn_exp2f(alog * LOG2E);
+    // log2 decay = lb log2(e) sigmoid(e^A_log (g + dt_bias)), with the exponent's
+    // -e^A_log log2(e) folded into one factor.
+    const float nEA = -__builtin_amdgcn_exp2f(alog * LOG2E) * LOG2E;
     const float lbm = p.lb_log2e * vmask;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      qv[i] *= vmask;
-      kv[i] *= vmask;
-      la[i] = lbm * sigmoid_f32(eA * (gv[i] + dt[i]));
-    }
+    for (int i = 0; i < 32; ++i)
+      la[i] = lbm * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f((gv[i] + dt[i]) * nEA));
   }
   float ssq = 0.f, ssk = 0.f;
 #pragma unroll
@@ -215,8 +214,10 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
   ssq += __shfl_xor(ssq, 32);
   ssk += __shfl_xor(ssk, 16);
   ssk += __shfl_xor(ssk, 32);
-  const float rq = __builtin_amdgcn_rsqf(ssq + L2_EPS);
-  const float rk = __builtin_amdgcn_rsqf(ssk + L2_EPS);
+  // Rows past the chunk end hold a copy of the last row; zeroing the norm factors zeroes
+  // every q and k product they feed.
+  const float rq = __builtin_amdgcn_rsqf(ssq + L2_EPS) * vmask;
+  const float rk = __builtin_amdgcn_rsqf(ssk + L2_EPS) * vmask;
   if (g == 0) sm.beta[t] = beta_t;
 
   // In-block inclusive cumulative log2 decay (lanes m = 0..15 of a row are 16 tokens).
@@ -281,14 +282,15 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
         const float Lf = __builtin_amdgcn_exp2f(la[i]);
         const float Rf = __builtin_amdgcn_exp2f(-la[i]);
         const float kh = kv[i] * rk;
-        const float qh = qv[i] * rq;
-        const float gam = ebv[i] * Lf;
-        kg[e] = static_cast<_Float16>(-kh * gam);
-        qg[e] = static_cast<_Float16>(qv[i] * rqs * gam);
-        kch[i] = static_cast<_Float16>(kcv[i] * Rf * kh);
-        klv[e] = kh * Lf;
-        qlv[e] = qh * Lf;
-        kv[i] = kh * Rf;  // the fp32 right factor, kept for publication
+        const float kl = kh * Lf;             // k^ 2^(b_t - base_w)
+        const float ql = qv[i] * rqs * Lf;    // scale q^ 2^(b_t - base_w)
+        const float kr = kh * Rf;             // k^ 2^(base_w - b_t)
+        kg[e] = static_cast<_Float16>(-kl * ebv[i]);
+        qg[e] = static_cast<_Float16>(ql * ebv[i]);
+        kch[i] = static_cast<_Float16>(kcv[i] * kr);
+        klv[e] = kl;
+        qlv[e] = ql;
+        kv[i] = kr;  // the fp32 right factor, kept for publication
       }
       u32x4 klp, qhp, qlp, rhp, rlp;
 #pragma unroll
@@ -376,7 +378,7 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
     for (int r = 0; r < 4; ++r) {
       const int tr = 16 * w + 4 * g + r;
       const float gval = bt[r] * accG[r];
-      const float pval = p.scale * accP[r];
+      const float pval = accP[r];   // the left factors carry the scale
       sm.AT[tr * ATS + i] = (i < tr) ? gval : 0.f;
       sm.P[tr * ATS + i] = (i <= tr) ? pval : 0.f;
     }
@@ -406,9 +408,15 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
     const float* Ab = sm.AT + (16 * w) * ATS + 16 * w;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
+      float a[16];
+#pragma unroll
+      for (int q4 = 0; q4 < (r + 3) / 4; ++q4) {
+        const float4 v4 = *reinterpret_cast<const float4*>(Ab + r * ATS + 4 * q4);
+        a[4 * q4] = v4.x; a[4 * q4 + 1] = v4.y; a[4 * q4 + 2] = v4.z; a[4 * q4 + 3] = v4.w;
+      }
       float acc = (r == j) ? 1.f : 0.f;
 #pragma unroll
-      for (int c = 0; c < r; ++c) acc -= Ab[r * ATS + c] * x[c];
+      for (int c = 0; c < r; ++c) acc -= a[c] * x[c];
       x[r] = acc;
     }
     // All lanes of this wave have read block (w, w) before any lane writes it.
