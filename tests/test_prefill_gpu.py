@@ -100,6 +100,19 @@ def test_prefill_ragged_varlen(lens, H, init):
     _compare(data, out, final)
 
 
+def test_prefill_many_short_sequences():
+    """120 sequences of 0..129 tokens: a deep chunk-map search, many chunk slots that
+    belong to no chunk, and the scan configuration for more pairs than CUs."""
+    lens = np.random.default_rng(3200).integers(0, 130, size=120).tolist()
+    case = W.PrefillCase("many_short_120_h2", lens, 2, init="per_seq", seed=3200)
+    print(f"case {case.name} tokens {sum(lens)}", flush=True)
+    data = W.make_prefill(case)
+    d = _dev(data)
+    out, final = _call(d)
+    torch.cuda.synchronize()
+    _compare(data, out, final)
+
+
 def test_prefill_pool_gather_and_bad_index():
     case = W.PrefillCase("pool_gather", [70, 100, 33], 2, init="pool", pool_slots=6, seed=3101)
     data = W.make_prefill(case)
