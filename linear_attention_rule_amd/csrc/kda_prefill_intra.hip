@@ -383,8 +383,10 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
       sm.P[tr * ATS + i] = (i <= tr) ? pval : 0.f;
     }
   }
-  for (int wb = w + 1; wb < 4; ++wb) {
-    const int i = 16 * wb + m;
+  // Above the diagonal only blocks (0, 1) and (2, 3) are ever read: the record's 32-deep
+  // k-steps of row blocks 0 and 2 span them.  The inverse reads the lower blocks only.
+  if ((w & 1) == 0) {
+    const int i = 16 * (w + 1) + m;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int tr = 16 * w + 4 * g + r;
