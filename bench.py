@@ -196,7 +196,7 @@ def summarize(prof_dirs, workload, out_md, mode_flag):
     lines = [f"# rocprofv3 summary: {workload}", "",
              "Commands (run from /tmp with TMPDIR=/tmp; R = repository root):", "",
              "    rocprofv3 --kernel-trace --stats --output-format csv -d OUT/prof_trace -o trace "
-             f"-- python3 $R/bench.py --steps 20 --warmup 5 --no-cpu-baseline {mode_flag}",
+             f"-- python3 $R/bench.py --no-cpu-baseline {mode_flag}",
              "    rocprofv3 --pmc FETCH_SIZE --kernel-trace --output-format csv -d OUT/prof_fetch "
              f"-o fetch -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline {mode_flag} "
              "--calib-copy",
