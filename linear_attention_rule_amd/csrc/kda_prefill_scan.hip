@@ -135,23 +135,33 @@ struct ChunkCopy {
       lds_dma16(rec + f * 1024u, lane_off, lds + f * 1024u);
     }
   }
-  // Pulls this wave's share of the chunk into L2 ahead of its copy: one dword per
-  // 128-byte line of the record share (lines past the record clamp to its last
-  // dword) and one per value-tile row (a wave without a value tile re-touches the
-  // record's last dword, so every wave issues NTOUCH), dropped into a 256-byte LDS
-  // sink that nothing reads.
-  static constexpr int NTOUCH = (PER * 8 + 63) / 64 + 1;
-  __device__ __forceinline__ void touch(int lane, uint32_t sink) const {
-#pragma unroll
-    for (int i = 0; i < NTOUCH - 1; ++i) {
-      const uint32_t off = min(static_cast<uint32_t>(f0 * 1024 + (64 * i + lane) * 128),
-                               static_cast<uint32_t>(REC_BYTES - 4));
-      lds_dma4(rec, off, sink);
-    }
+  // Pulls this workgroup's share of chunk jj's record into L2 ahead of its copy: the
+  // workgroups that read the same records (nshare of them) each touch one dword per
+  // 128-byte line of their own part of it, split over the NC copy waves, plus one dword
+  // per value-tile row of their own slice (a wave without a value tile re-touches a
+  // line of its part), dropped into a 256-byte LDS sink that nothing reads.  Every
+  // workgroup touching the whole record instead ran slower than no touch at all (copy
+  // probe on MI355X, 64 records per step shared four ways: 3430 cycles per step without
+  // touches, 4680 touching the whole record, 2150 touching a quarter each).
+  static constexpr int REC_LINES = (REC_BYTES + 127) / 128;
+  static constexpr int MIN_SHARE = D / (16 * NB * NC);   // value slices: fewest sharers
+  static constexpr int NTOUCH_REC = ((REC_LINES + MIN_SHARE - 1) / MIN_SHARE + NC - 1) / NC;
+  static_assert(NTOUCH_REC <= 64, "one touch instruction per copy wave");
+  static constexpr int NTOUCH = 2;
+  __device__ __forceinline__ void touch(int lane, uint32_t sink, int c, int share,
+                                        int nshare) const {
+    const int per_wg = (REC_LINES + nshare - 1) / nshare;
+    const int per_wave = (per_wg + NC - 1) / NC;
+    const int first = min(share * per_wg + c * per_wave, REC_LINES - 1);
+    const int last = min(min(share * per_wg + (c + 1) * per_wave, (share + 1) * per_wg),
+                         REC_LINES) - 1;
+    const int line = min(first + lane, max(last, first));
+    const uint32_t off = min(static_cast<uint32_t>(line * 128), static_cast<uint32_t>(REC_BYTES - 4));
+    lds_dma4(rec, off, sink);
     if (has_vt)
       lds_dma4(vt, vrow_lane, sink);
     else
-      lds_dma4(rec, static_cast<uint32_t>(REC_BYTES - 4), sink);
+      lds_dma4(rec, off, sink);
   }
   uint32_t vrow_lane;
 };
@@ -315,6 +325,7 @@ constexpr int START_WS = 3;      // a state in the segment workspace
 
 struct ScanWork {
   int n, h, vs, jb, je;          // sequence, head, value slice, chunks [jb, je)
+  int share, nshare;             // this workgroup's index among those reading the same records
   int start;
   const float* start_blk;        // START_WS: the [128][128] start state
   float* fin_blk;                // [128][128] destination of the end state, or null
@@ -366,6 +377,8 @@ __device__ __forceinline__ bool decode_work(const PrefillParams& p, ScanWork& wk
   wk.start_blk = nullptr;
   wk.zero_v = false;
   wk.write_out = true;
+  wk.share = cg;
+  wk.nshare = NVS;
   if (MODE == MODE_SEQ) {
     wk.vs = cg;
     wk.jb = 0;
@@ -387,6 +400,7 @@ __device__ __forceinline__ bool decode_work(const PrefillParams& p, ScanWork& wk
       return true;
     }
     wk.write_out = false;
+    wk.nshare = 2 * NVS;                 // the map and offset workgroups read the same records
     if (cg < NVS) {                      // the map M_s: identity columns, no values
       wk.vs = cg;
       wk.start = START_IDENT;
@@ -460,8 +474,9 @@ void prefill_scan_kernel(PrefillParams p) {
     // that wait, so their write acknowledgements stay off this chunk's critical path.
     using CC = ChunkCopy<NC, NB>;
     // The touch-ahead pays off with four workgroups per pair (two compute waves each:
-    // 4 x 8192 x 16 heads, 258 -> 253 us) and costs with two (four compute waves: 8 x 2048
-    // x 16 heads, 91 -> 96 us), so only the former issues it.
+    // 4 x 8192 x 16 heads, 259 -> 194 us; 1 x 16384 segmented, 238 -> 210 us), where the
+    // copies bound the chunk step.  With two (four compute waves: 8 x 2048 x 16 heads,
+    // 90 us either way) the compute does, so it is left out there.
     constexpr bool TOUCH = (NW == 2);
     const bool copy_vt = has_vt && !wk.zero_v;
     const bool store = has_vt && wk.write_out;
@@ -473,7 +488,7 @@ void prefill_scan_kernel(PrefillParams p) {
         CC(p, recbase, cs, ce, jb, h, v0, cw, copy_vt, lane, lds0, vt_off).all();
         if (TOUCH) {
           CC(p, recbase, cs, ce, min(jb + 1, je - 1), h, v0, cw, copy_vt, lane, lds1, vt_off)
-              .touch(lane, sink);
+              .touch(lane, sink, cw, wk.share, wk.nshare);
           asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CC::NTOUCH) : "memory");
         } else {
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -489,7 +504,7 @@ void prefill_scan_kernel(PrefillParams p) {
         CC(p, recbase, cs, ce, j + 1, h, v0, cw, copy_vt, lane, par ? lds0 : lds1, vt_off).all();
         if (TOUCH) {
           CC(p, recbase, cs, ce, min(j + 2, je - 1), h, v0, cw, copy_vt, lane, lds0, vt_off)
-              .touch(lane, sink);
+              .touch(lane, sink, cw, wk.share, wk.nshare);
           asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CC::NTOUCH) : "memory");
         } else {
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
