@@ -210,32 +210,53 @@ __device__ __forceinline__ void scan_chunk(const unsigned char* __restrict__ R,
                                            bool write_out, int lane, f32x4 (&S)[NB][8]) {
   const int nl = lane & 15, g = lane >> 4;
   const uint16_t* vt = reinterpret_cast<const uint16_t*>(VT);
+  // Stage 1: every LDS read of the X and U products goes out before the first MFMA.
+  uint16_t vraw[NB][4][4];
+  half8 kgf[16], tpf[6];
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vraw[nb][tb][r] = vt[(16 * tb + 4 * g + r) * (16 * NB) + 16 * nb + nl];
+#pragma unroll
+  for (int f = 0; f < 16; ++f) kgf[f] = frag(R, FR_KG + f, lane);
+#pragma unroll
+  for (int f = 0; f < 6; ++f) tpf[f] = frag(R, FR_TP + f, lane);
+  __builtin_amdgcn_sched_barrier(0);
+
   half8 Sf[NB][4];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int s = 0; s < 4; ++s) Sf[nb][s] = pack_f16(S[nb][2 * s], S[nb][2 * s + 1]);
-
-  // X = V - K_Gamma S   (rows = tokens, lane column = value channel)
   f32x4 X[NB][4];
 #pragma unroll
-  for (int tb = 0; tb < 4; ++tb) {
+  for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tt = 16 * tb + 4 * g + r;
-        const float vv = bf16_to_f32(vt[tt * (16 * NB) + 16 * nb + nl]);
-        X[nb][tb][r] = (tt < Lc && !zero_v) ? vv : 0.f;
+        X[nb][tb][r] = (tt < Lc && !zero_v) ? bf16_to_f32(vraw[nb][tb][r]) : 0.f;
       }
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const half8 a = frag(R, FR_KG + 4 * tb + s, lane);
+  for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) X[nb][tb] = mfma_f16(a, Sf[nb][s], X[nb][tb]);
-    }
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) X[nb][tb] = mfma_f16(kgf[4 * tb + s], Sf[nb][s], X[nb][tb]);
+
+  // Stage 2 reads (the output products' operands) go out behind the X products.
+  half8 qgf[16], pmf[6];
+  if (write_out) {
+#pragma unroll
+    for (int f = 0; f < 16; ++f) qgf[f] = frag(R, FR_QG + f, lane);
+#pragma unroll
+    for (int f = 0; f < 6; ++f) pmf[f] = frag(R, FR_PM + f, lane);
   }
-  // U = T' X
+  __builtin_amdgcn_sched_barrier(0);
+
   half8 Xf[NB][2];
   f32x4 U[NB][4];
 #pragma unroll
@@ -245,19 +266,14 @@ __device__ __forceinline__ void scan_chunk(const unsigned char* __restrict__ R,
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) U[nb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  {
-    const half8 t0 = frag(R, FR_TP + 0, lane), t1 = frag(R, FR_TP + 1, lane);
-    const half8 t2 = frag(R, FR_TP + 2, lane), t3 = frag(R, FR_TP + 3, lane);
-    const half8 t4 = frag(R, FR_TP + 4, lane), t5 = frag(R, FR_TP + 5, lane);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      U[nb][0] = mfma_f16(t0, Xf[nb][0], U[nb][0]);
-      U[nb][1] = mfma_f16(t1, Xf[nb][0], U[nb][1]);
-      U[nb][2] = mfma_f16(t2, Xf[nb][0], U[nb][2]);
-      U[nb][2] = mfma_f16(t3, Xf[nb][1], U[nb][2]);
-      U[nb][3] = mfma_f16(t4, Xf[nb][0], U[nb][3]);
-      U[nb][3] = mfma_f16(t5, Xf[nb][1], U[nb][3]);
-    }
+  for (int nb = 0; nb < NB; ++nb) {
+    U[nb][0] = mfma_f16(tpf[0], Xf[nb][0], U[nb][0]);
+    U[nb][1] = mfma_f16(tpf[1], Xf[nb][0], U[nb][1]);
+    U[nb][2] = mfma_f16(tpf[2], Xf[nb][0], U[nb][2]);
+    U[nb][2] = mfma_f16(tpf[3], Xf[nb][1], U[nb][2]);
+    U[nb][3] = mfma_f16(tpf[4], Xf[nb][0], U[nb][3]);
+    U[nb][3] = mfma_f16(tpf[5], Xf[nb][1], U[nb][3]);
   }
   half8 Uf[NB][2];
 #pragma unroll
@@ -274,21 +290,15 @@ __device__ __forceinline__ void scan_chunk(const unsigned char* __restrict__ R,
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const half8 bq = frag(R, FR_QG + 4 * tb + s, lane);
+      for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) o[nb] = mfma_f16(Sf[nb][s], bq, o[nb]);
-      }
+        for (int nb = 0; nb < NB; ++nb) o[nb] = mfma_f16(Sf[nb][s], qgf[4 * tb + s], o[nb]);
       const int fi = (tb < 2) ? tb : 2 + 2 * (tb - 2);
-      {
-        const half8 bp = frag(R, FR_PM + fi, lane);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) o[nb] = mfma_f16(Uf[nb][0], bp, o[nb]);
-      }
+      for (int nb = 0; nb < NB; ++nb) o[nb] = mfma_f16(Uf[nb][0], pmf[fi], o[nb]);
       if (tb >= 2) {
-        const half8 bp = frag(R, FR_PM + fi + 1, lane);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) o[nb] = mfma_f16(Uf[nb][1], bp, o[nb]);
+        for (int nb = 0; nb < NB; ++nb) o[nb] = mfma_f16(Uf[nb][1], pmf[fi + 1], o[nb]);
       }
       uint16_t* orow = SO + (16 * tb + nl) * (16 * NB) + 4 * g;
 #pragma unroll
@@ -297,20 +307,27 @@ __device__ __forceinline__ void scan_chunk(const unsigned char* __restrict__ R,
             make_uint2(pack_bf16x2(o[nb][0], o[nb][1]), pack_bf16x2(o[nb][2], o[nb][3]));
     }
   }
-  // S <- Diag(Gamma_C) S + K_C^T U
+  // Stage 3 reads (the state update's operands) go out behind the output products.
+  half8 kcf[16];
+  float4 gcv[8];
   const float* gam = reinterpret_cast<const float*>(R + REC_GAMMA_OFF);
 #pragma unroll
+  for (int f = 0; f < 16; ++f) kcf[f] = frag(R, FR_KC + f, lane);
+#pragma unroll
+  for (int cb = 0; cb < 8; ++cb) gcv[cb] = *reinterpret_cast<const float4*>(gam + 16 * cb + 4 * g);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // S <- Diag(Gamma_C) S + K_C^T U
+#pragma unroll
   for (int cb = 0; cb < 8; ++cb) {
-    const float4 gc = *reinterpret_cast<const float4*>(gam + 16 * cb + 4 * g);
-    const half8 k0 = frag(R, FR_KC + 2 * cb + 0, lane), k1 = frag(R, FR_KC + 2 * cb + 1, lane);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      S[nb][cb][0] *= gc.x;
-      S[nb][cb][1] *= gc.y;
-      S[nb][cb][2] *= gc.z;
-      S[nb][cb][3] *= gc.w;
-      S[nb][cb] = mfma_f16(k0, Uf[nb][0], S[nb][cb]);
-      S[nb][cb] = mfma_f16(k1, Uf[nb][1], S[nb][cb]);
+      S[nb][cb][0] *= gcv[cb].x;
+      S[nb][cb][1] *= gcv[cb].y;
+      S[nb][cb][2] *= gcv[cb].z;
+      S[nb][cb][3] *= gcv[cb].w;
+      S[nb][cb] = mfma_f16(kcf[2 * cb], Uf[nb][0], S[nb][cb]);
+      S[nb][cb] = mfma_f16(kcf[2 * cb + 1], Uf[nb][1], S[nb][cb]);
     }
   }
 }
