@@ -199,6 +199,32 @@ __device__ __forceinline__ void store_out_tile(const PrefillParams& p, const uin
   }
 }
 
+// The store wave's variant: the NW output tiles of a chunk (one per compute wave, 16 NB
+// columns each, side by side in the output row) stored together, so each lane's 16 bytes
+// and its row neighbours form one contiguous 32 NB NW-byte run per row (fewer, longer
+// row segments per store instruction than one tile at a time).
+template <int NB, int NW>
+__device__ __forceinline__ void store_out_tiles(const PrefillParams& p,
+                                                const uint16_t (*so)[64 * 16 * NB],
+                                                const int* sidx, int cs, int ce, int jj, int h,
+                                                int vbase, int lane) {
+  constexpr int TCOLS = 16 * NB;                 // columns of one tile
+  constexpr int LPR = NW * TCOLS * 2 / 16;        // lanes per output row
+  constexpr int RPI = 64 / LPR;                   // rows per store instruction
+  const int tbj = cs + jj * CHUNK;
+  const int Lc = min(CHUNK, ce - tbj);
+  const int q = lane % LPR;                       // 16-byte piece of the row
+  const int tile = q / (TCOLS / 8), tc = 8 * (q % (TCOLS / 8));
+#pragma unroll
+  for (int i = 0; i < 64 / RPI; ++i) {
+    const int row = lane / LPR + RPI * i;
+    const uint4 val = *reinterpret_cast<const uint4*>(so[tile] + row * TCOLS + tc);
+    const int64_t orow = p.out_idx ? static_cast<int64_t>(sidx[row]) : tbj + row;
+    if (row < Lc && orow >= 0 && orow < p.out_rows)
+      *reinterpret_cast<uint4*>(p.out + orow * p.o_st + h * D + vbase + 8 * q) = val;
+  }
+}
+
 // One chunk of the state scan for NB 16-column blocks of this wave, reading the record
 // from LDS buffer R and writing the chunk's output rows (bf16, 64 x 16 NB, row-major,
 // rows past the chunk end included) to the LDS tile SO.  Every fragment read from LDS
@@ -500,19 +526,14 @@ void prefill_scan_kernel(PrefillParams p) {
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       if (j > jb && wk.write_out)
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww)
-          store_out_tile<NB>(p, sout[par ^ 1][ww], sidx[par ^ 1], cs, ce, j - 1, h,
-                             wk.vs * BV + 16 * NB * ww, lane);
+        store_out_tiles<NB, NW>(p, sout[par ^ 1], sidx[par ^ 1], cs, ce, j - 1, h, wk.vs * BV,
+                                lane);
     }
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (je > jb && wk.write_out) {
       const int par = (je - 1 - jb) & 1;
-#pragma unroll
-      for (int ww = 0; ww < NW; ++ww)
-        store_out_tile<NB>(p, sout[par][ww], sidx[par], cs, ce, je - 1, h,
-                           wk.vs * BV + 16 * NB * ww, lane);
+      store_out_tiles<NB, NW>(p, sout[par], sidx[par], cs, ce, je - 1, h, wk.vs * BV, lane);
     }
     return;
   }
