@@ -149,7 +149,7 @@ struct ChunkCopy {
   static_assert(NTOUCH_REC <= 64, "one touch instruction per copy wave");
   static constexpr int NTOUCH = 2;
   __device__ __forceinline__ void touch(int lane, uint32_t sink, int c, int share,
-                                        int nshare) const {
+                                        int nshare, bool touch_v) const {
     const int per_wg = (REC_LINES + nshare - 1) / nshare;
     const int per_wave = (per_wg + NC - 1) / NC;
     const int first = min(share * per_wg + c * per_wave, REC_LINES - 1);
@@ -158,7 +158,7 @@ struct ChunkCopy {
     const int line = min(first + lane, max(last, first));
     const uint32_t off = min(static_cast<uint32_t>(line * 128), static_cast<uint32_t>(REC_BYTES - 4));
     lds_dma4(rec, off, sink);
-    if (has_vt)
+    if (touch_v)
       lds_dma4(vt, vrow_lane, sink);
     else
       lds_dma4(rec, off, sink);
@@ -553,6 +553,9 @@ void prefill_scan_kernel(PrefillParams p) {
     // 90 us either way) the compute does, so it is left out there.
     constexpr bool TOUCH = (NW == 2);
     const bool copy_vt = has_vt && !wk.zero_v;
+    // One wave touches each 128-byte line of value rows: the two 64-byte halves of a
+    // line belong to value slices 2k and 2k+1, and a workgroup's copy waves share it.
+    const bool touch_v = copy_vt && cw == 0 && (wk.vs & 1) == 0;
     const bool store = has_vt && wk.write_out;
     const uint32_t lds0 = lds_addr(srec0), lds1 = lds_addr(srec1);
     const uint32_t sink = lds_addr(touch_sink[cw]);
@@ -562,7 +565,7 @@ void prefill_scan_kernel(PrefillParams p) {
         CC(p, recbase, cs, ce, jb, h, v0, cw, copy_vt, lane, lds0, vt_off).all();
         if (TOUCH) {
           CC(p, recbase, cs, ce, min(jb + 1, je - 1), h, v0, cw, copy_vt, lane, lds1, vt_off)
-              .touch(lane, sink, cw, wk.share, wk.nshare);
+              .touch(lane, sink, cw, wk.share, wk.nshare, touch_v);
           asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CC::NTOUCH) : "memory");
         } else {
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -578,7 +581,7 @@ void prefill_scan_kernel(PrefillParams p) {
         CC(p, recbase, cs, ce, j + 1, h, v0, cw, copy_vt, lane, par ? lds0 : lds1, vt_off).all();
         if (TOUCH) {
           CC(p, recbase, cs, ce, min(j + 2, je - 1), h, v0, cw, copy_vt, lane, lds0, vt_off)
-              .touch(lane, sink, cw, wk.share, wk.nshare);
+              .touch(lane, sink, cw, wk.share, wk.nshare, touch_v);
           asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CC::NTOUCH) : "memory");
         } else {
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
