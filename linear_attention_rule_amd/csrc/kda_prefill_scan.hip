@@ -114,12 +114,16 @@ struct ChunkCopy {
     const int Lc = min(CHUNK, ce - tbj);
     vt = uniform_addr(p.v + static_cast<int64_t>(tbj) * p.v_st + h * D + v0);
     lds = lds_;
-    vlds = lds_ + static_cast<uint32_t>(vt_off);
+    vlds = lds_ + static_cast<uint32_t>(vt_off + c * VTl::COPIES * 1024);
     lane_off = static_cast<uint32_t>(lane * 16);
+    // The value tiles of all compute waves form one [64][16 NB NC] tile (rows of
+    // 32 NB NC bytes); copy wave c issues its instructions c*COPIES .. c*COPIES+COPIES-1,
+    // each 16 bytes per lane, so rows go out as runs of that length.
+    constexpr int LPR = 2 * NB * NC, RPI = 64 / LPR;
 #pragma unroll
     for (int i = 0; i < VTl::COPIES; ++i) {
-      const int row = min(lane / VTl::LANES_PER_ROW + VTl::ROWS_PER_COPY * i, Lc - 1);
-      voff[i] = static_cast<uint32_t>((row * p.v_st + 8 * (lane % VTl::LANES_PER_ROW)) * 2);
+      const int row = min(lane / LPR + RPI * (c * VTl::COPIES + i), Lc - 1);
+      voff[i] = static_cast<uint32_t>((row * p.v_st + 8 * (lane % LPR)) * 2);
     }
     f0 = c * PER;
     vrow_lane = static_cast<uint32_t>(min(lane, Lc - 1) * p.v_st * 2);
@@ -229,9 +233,9 @@ __device__ __forceinline__ void store_out_tiles(const PrefillParams& p,
 // from LDS buffer R and writing the chunk's output rows (bf16, 64 x 16 NB, row-major,
 // rows past the chunk end included) to the LDS tile SO.  Every fragment read from LDS
 // feeds NB MFMAs.
-template <int NB>
+template <int NB, int NW>
 __device__ __forceinline__ void scan_chunk(const unsigned char* __restrict__ R,
-                                           const unsigned char* __restrict__ VT,
+                                           const unsigned char* __restrict__ VT, int vcol,
                                            uint16_t* __restrict__ SO, int Lc, bool zero_v,
                                            bool write_out, int lane, f32x4 (&S)[NB][8]) {
   const int nl = lane & 15, g = lane >> 4;
@@ -244,7 +248,8 @@ __device__ __forceinline__ void scan_chunk(const unsigned char* __restrict__ R,
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) vraw[nb][tb][r] = vt[(16 * tb + 4 * g + r) * (16 * NB) + 16 * nb + nl];
+      for (int r = 0; r < 4; ++r)
+        vraw[nb][tb][r] = vt[(16 * tb + 4 * g + r) * (16 * NB * NW) + vcol + 16 * nb + nl];
 #pragma unroll
   for (int f = 0; f < 16; ++f) kgf[f] = frag(R, FR_KG + f, lane);
 #pragma unroll
@@ -489,6 +494,7 @@ __attribute__((amdgpu_waves_per_eu((NW + NC + store_waves<NW>() + 3) / 4,
                                    (NW + NC + store_waves<NW>() + 3) / 4)))
 void prefill_scan_kernel(PrefillParams p) {
   using VTl = VTile<NB>;
+  static_assert(NC == NW, "each copy wave fills its share of the combined value tile");
   constexpr int BUF_BYTES = REC_BYTES + NW * VTl::BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char srec0[BUF_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char srec1[BUF_BYTES];
@@ -515,7 +521,7 @@ void prefill_scan_kernel(PrefillParams p) {
   const int len = ce - cs;
   const int64_t slot0 = cs / CHUNK + n;
   const unsigned char* recbase = p.work + (slot0 * H + h) * REC_BYTES;
-  const int vt_off = REC_BYTES + w * VTl::BYTES;
+  const int vt_off = REC_BYTES;                // the combined value tile
 
   if (STORE_WAVE && storer) {
     // The store wave: after each chunk's barrier, the previous chunk's output tiles
@@ -562,9 +568,9 @@ void prefill_scan_kernel(PrefillParams p) {
     for (int j = jb; j < je; ++j) {
       const int par = (j - jb) & 1;
       if (j == jb) {
-        CC(p, recbase, cs, ce, jb, h, v0, cw, copy_vt, lane, lds0, vt_off).all();
+        CC(p, recbase, cs, ce, jb, h, wk.vs * BV, cw, copy_vt, lane, lds0, vt_off).all();
         if (TOUCH) {
-          CC(p, recbase, cs, ce, min(jb + 1, je - 1), h, v0, cw, copy_vt, lane, lds1, vt_off)
+          CC(p, recbase, cs, ce, min(jb + 1, je - 1), h, wk.vs * BV, cw, copy_vt, lane, lds1, vt_off)
               .touch(lane, sink, cw, wk.share, wk.nshare, touch_v);
           asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CC::NTOUCH) : "memory");
         } else {
@@ -578,9 +584,9 @@ void prefill_scan_kernel(PrefillParams p) {
       if (wk.write_out && p.out_idx && cw == 0)
         copy_out_index(p, cs, ce, j, lane, lds_addr(sidx[par]));
       if (j + 1 < je) {
-        CC(p, recbase, cs, ce, j + 1, h, v0, cw, copy_vt, lane, par ? lds0 : lds1, vt_off).all();
+        CC(p, recbase, cs, ce, j + 1, h, wk.vs * BV, cw, copy_vt, lane, par ? lds0 : lds1, vt_off).all();
         if (TOUCH) {
-          CC(p, recbase, cs, ce, min(j + 2, je - 1), h, v0, cw, copy_vt, lane, lds0, vt_off)
+          CC(p, recbase, cs, ce, min(j + 2, je - 1), h, wk.vs * BV, cw, copy_vt, lane, lds0, vt_off)
               .touch(lane, sink, cw, wk.share, wk.nshare, touch_v);
           asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CC::NTOUCH) : "memory");
         } else {
@@ -641,13 +647,13 @@ void prefill_scan_kernel(PrefillParams p) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    scan_chunk<NB>(srec0, srec0 + vt_off, sout[0][w], min(CHUNK, len - j * CHUNK), wk.zero_v,
+    scan_chunk<NB, NW>(srec0, srec0 + vt_off, 16 * NB * w, sout[0][w], min(CHUNK, len - j * CHUNK), wk.zero_v,
                    wk.write_out, lane, S);
     if (j + 1 >= je) break;
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    scan_chunk<NB>(srec1, srec1 + vt_off, sout[1][w], min(CHUNK, len - (j + 1) * CHUNK),
+    scan_chunk<NB, NW>(srec1, srec1 + vt_off, 16 * NB * w, sout[1][w], min(CHUNK, len - (j + 1) * CHUNK),
                    wk.zero_v, wk.write_out, lane, S);
   }
   // Output tiles of the last chunk complete before the copy waves store them.
