@@ -9,9 +9,10 @@
 //   pairing 16-row blocks (2s, 2s+1) into one 32-deep k-step, so no shuffles are
 //   needed; the record fragments carry the matching k order.  Copy waves, one
 //   per compute wave, double-buffer the records in LDS with
-//   global_load_lds_dwordx4, pull the chunk after next into L2, and store the
-//   output tiles the compute waves leave in LDS, so the compute waves run only
-//   LDS reads and MFMAs while the next chunk is in flight.
+//   global_load_lds_dwordx4 and pull this workgroup's share of the chunk after
+//   next into L2; the output tiles the compute waves leave in LDS are stored by a
+//   store wave (two compute waves) or by the copy waves (four), so the compute
+//   waves run only LDS reads and MFMAs while the next chunk is in flight.
 #include <algorithm>
 
 #include "kda_prefill_common.h"
@@ -23,8 +24,9 @@ namespace {
 using namespace prefill;
 
 // 16-column value blocks per scan compute wave.  One copy wave per compute wave:
-// more copy waves do not raise a CU's copy rate (measured on MI355X: 2 compute
-// waves with 4 or 6 copy waves took 292 and 328 us at 4x8192 x16 heads, vs 283).
+// more copy waves do not raise a CU's copy rate (measured on MI355X at 4x8192 x16
+// heads: 2 compute waves with 4 or 6 copy waves took 292 and 328 us against 283
+// before the shared touch-ahead, and 4 took 206-209 against 201-204 us after it).
 constexpr int SCAN_NB = 1;
 
 // 16 bytes per lane from global memory straight into LDS (no VGPR staging):
@@ -87,9 +89,9 @@ struct VTile {
 // The copies copy wave c of NC issues to bring chunk jj into an LDS buffer: its share
 // of the chunk record (the contiguous 1 KiB fragments [c*PER, (c+1)*PER); all issue the
 // same compile-time count, surplus copies repeating the last fragment with identical
-// bytes) and, when it serves a compute wave (has_vt), that wave's value tile (16 bytes
-// per lane per copy, rows in order; rows past the chunk end re-read the last valid
-// row, in bounds, whose values only ever meet zero columns of T' and are never stored).
+// bytes) and, when has_vt, its share of the workgroup's value tile (16 bytes per lane
+// per copy, rows in order; rows past the chunk end re-read the last valid row, in
+// bounds, whose values only ever meet zero columns of T' and are never stored).
 template <int NC, int NB>
 struct ChunkCopy {
   using VTl = VTile<NB>;
@@ -473,16 +475,17 @@ __device__ __forceinline__ bool decode_work(const PrefillParams& p, ScanWork& wk
   return true;
 }
 
-// Workgroup: NW compute waves (wave w owns value columns v0 .. v0 + 16 NB) and NC >= NW
-// copy waves (copy wave c < NW serves compute wave c's value and output tiles).  A wave
-// that issues a whole chunk's copies stalls at issue until the copy engine has drained
-// most of them, and copies issued piecemeal during the compute land too late; so all
-// vector-memory work goes to waves of their own: they issue a chunk's copies at once at
-// the start of the previous chunk and wait for them, and store the output tiles the
-// compute waves leave in LDS.  The compute waves only read LDS and run MFMAs.  One
-// barrier per chunk plus a final one: when every wave has reached the barrier of chunk
-// j, chunk j has landed in buffer (j - jb) % 2, chunk j-1's buffer is free and chunk
-// j-1's output tiles are complete.
+// Workgroup: NW compute waves (wave w owns value columns v0 .. v0 + 16 NB), NC = NW copy
+// waves (each copies its share of the record and of the combined value tile; without a
+// store wave, copy wave c stores compute wave c's output tile) and, with two compute
+// waves, a store wave.  A wave that issues a whole chunk's copies stalls at issue until
+// the copy engine has drained most of them, and copies issued piecemeal during the
+// compute land too late; so all vector-memory work goes to waves of their own: they
+// issue a chunk's copies at once at the start of the previous chunk and wait for them,
+// and store the output tiles the compute waves leave in LDS.  The compute waves only
+// read LDS and run MFMAs.  One barrier per chunk plus a final one: when every wave has
+// reached the barrier of chunk j, chunk j has landed in buffer (j - jb) % 2, chunk j-1's
+// buffer is free and chunk j-1's output tiles are complete.
 // With two compute waves the copy waves bound the chunk step, and a separate store wave
 // takes the output stores off them; with four the compute does, and the copy waves store.
 template <int NW>
@@ -511,7 +514,7 @@ void prefill_scan_kernel(PrefillParams p) {
   const bool storer = STORE_WAVE && wave == NW + NC;
   const bool copier = wave >= NW && !storer;
   const int cw = wave - NW;                  // copy wave index
-  const bool has_vt = cw < NW;               // copy wave serves compute wave cw
+  const bool has_vt = cw < NW;               // every copy wave (NC = NW) copies value rows
   const int w = copier ? (has_vt ? cw : 0) : wave;   // compute wave served / owned
   const int lane = tid & 63, nl = lane & 15, g = lane >> 4;
   const int H = p.H;
