@@ -133,6 +133,35 @@ def test_prefill_lower_bound_values(lb):
     _compare(data, out, final)
 
 
+def _saturate(data):
+    """Degenerate values in place: all-zero q or k rows (the l2 norm's epsilon case), gate
+    logits far past both ends of the sigmoid (decay pinned at the lower bound, or none at
+    all) over runs longer than a chunk, and beta logits that give beta = 1 or beta ~ 0."""
+    T = data["q"].shape[0]
+    t = torch.arange(T)
+    data["q"][t % 11 == 3] = 0
+    data["k"][t % 13 == 5] = 0
+    data["g"][(t >= 20) & (t < 150), 0] = 64.0      # head 0: decay at the bound for 130 tokens
+    data["g"][(t >= 160) & (t < 230), 1] = -64.0    # head 1: no decay for 70 tokens
+    data["g"][(t >= 600) & (t < 1400), 0] = 64.0    # long runs span whole scan segments
+    data["g"][(t >= 1500) & (t < 2500), 1] = -64.0
+    data["beta_logits"][t % 7 == 0] = 32.0
+    data["beta_logits"][t % 7 == 1] = -32.0
+
+
+@pytest.mark.parametrize("lens", [[230, 1, 97], [64 * 40 + 17]])   # the second: segmented scan
+def test_prefill_saturated_and_degenerate_inputs(lens):
+    case = W.PrefillCase("saturated", lens, 2, init="per_seq", seed=3106)
+    print(f"case {case.name} lens {case.seq_lens}", flush=True)
+    data = W.make_prefill(case)
+    _saturate(data)
+    d = _dev(data)
+    out, final = _call(d)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(final).all()
+    _compare(data, out, final)
+
+
 def test_prefill_writes_only_its_rows_and_handles_empty():
     case = W.PrefillCase("canary", [0, 77, 0], 2, init="per_seq", seed=3103)
     data = W.make_prefill(case)

@@ -71,6 +71,25 @@ def test_verify_1x8_latency_case():
     _check(data, out, inter)
 
 
+def test_verify_saturated_and_degenerate_inputs():
+    """Zero q or k rows, gate logits past both ends of the sigmoid and beta at 1 or ~0."""
+    data = W.make_verify(W.VerifyCase("saturated", 12, 8, 2, 16, seed=4106))
+    n = data["q"].shape[0]
+    t = torch.arange(n)
+    data["q"][t % 11 == 3] = 0
+    data["k"][t % 13 == 5] = 0
+    data["g"][t % 4 == 0, 0] = 64.0
+    data["g"][t % 4 == 1, 1] = -64.0
+    data["beta_logits"][t % 7 == 0] = 32.0
+    data["beta_logits"][t % 7 == 1] = -32.0
+    print("case saturated B 12 T 8 H 2", flush=True)
+    d = _dev(data)
+    out, inter = _call(d)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(inter).all()
+    _check(data, out, inter)
+
+
 @pytest.mark.parametrize("B,T,H", [(3, 1, 1), (5, 3, 2), (2, 16, 3), (1, 64, 2), (40, 8, 8)])
 def test_verify_small_shapes(B, T, H):
     case = W.VerifyCase(f"v_{B}x{T}_h{H}", B, T, H, pool_slots=B + 5, seed=2000 + B * 100 + T + H)
