@@ -162,6 +162,42 @@ def test_prefill_saturated_and_degenerate_inputs(lens):
     _compare(data, out, final)
 
 
+def _random_prefill_case(seed):
+    """A seeded random call shape: sequence lengths mixing the chunk boundaries (0, 1, 63,
+    64, 65, 127-129) with arbitrary lengths and, at times, one long enough for the
+    segment-parallel scan; 1-4 heads; zero, per-sequence or pooled start states; one of
+    the supported lower bounds."""
+    rng = np.random.default_rng(seed)
+    pick = [0, 1, 63, 64, 65, 127, 128, 129]
+    lens = []
+    for _ in range(int(rng.integers(1, 7))):
+        r = rng.random()
+        lens.append(int(rng.choice(pick)) if r < 0.4 else
+                    int(rng.integers(2, 300)) if r < 0.9 else int(rng.integers(1000, 2600)))
+    H = int(rng.integers(1, 5))
+    init = [None, "per_seq", "pool"][int(rng.integers(0, 3))]
+    lb = float(rng.choice([-5.0, -2.5, -1.0, 0.0]))
+    return W.PrefillCase(f"rand_{seed}", lens, H, init=init, pool_slots=len(lens) + 2,
+                         seed=seed, lower_bound=lb)
+
+
+@pytest.mark.parametrize("seed", range(3300, 3316))
+def test_prefill_random_shapes(seed):
+    case = _random_prefill_case(seed)
+    print(f"case {case.name} lens {case.seq_lens} H {case.heads} init {case.init} "
+          f"lb {case.lower_bound}", flush=True)
+    data = W.make_prefill(case)
+    if case.init == "pool":
+        # some sequences start from zero: a negative index or one past the pool
+        idx = data["initial_state_idx"]
+        idx[::3] = -1
+        idx[1::4] = case.pool_slots
+    d = _dev(data)
+    out, final = _call(d)
+    torch.cuda.synchronize()
+    _compare(data, out, final)
+
+
 def test_prefill_writes_only_its_rows_and_handles_empty():
     case = W.PrefillCase("canary", [0, 77, 0], 2, init="per_seq", seed=3103)
     data = W.make_prefill(case)

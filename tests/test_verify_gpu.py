@@ -100,6 +100,28 @@ def test_verify_small_shapes(B, T, H):
     _check(data, out, inter)
 
 
+@pytest.mark.parametrize("seed", range(4300, 4306))
+def test_verify_random_shapes(seed):
+    """Seeded random shapes: 1-20 rows, 1-16 draft steps (64 at times), 1-6 heads, a few
+    padding rows, and a pool of states larger than the batch."""
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 21))
+    T = 64 if rng.random() < 0.15 else int(rng.integers(1, 17))
+    H = int(rng.integers(1, 7))
+    pad = sorted(set(int(x) for x in rng.integers(0, B, size=int(rng.integers(0, 3)))))
+    if len(pad) == B:
+        pad = pad[:-1]
+    case = W.VerifyCase(f"vrand_{seed}", B, T, H, pool_slots=B + 3, seed=seed, padding_rows=pad)
+    print(f"case {case.name} B {B} T {T} H {H} padding {pad}", flush=True)
+    data = W.make_verify(case)
+    d = _dev(data)
+    out, inter = _call(d)
+    torch.cuda.synchronize()
+    _check(data, out, inter)
+    for b in pad:   # padding rows: zero outputs
+        assert torch.count_nonzero(out[b * T:(b + 1) * T]) == 0
+
+
 def test_verify_padding_rows_untouched():
     case = W.VerifyCase("v_pad", 6, 4, 2, pool_slots=8, seed=2101, padding_rows=[1])
     data = W.make_verify(case)
