@@ -175,6 +175,7 @@ kda_status kda_chunk_prefill_scan(const void* q, const void* k, const void* v, c
  *                   after token t of row b (0-based), so row (b, T-1) is the
  *                   state with every draft token accepted.  Must not overlap the pool.
  *   out             bf16 [B*T, H, 128]
+ * B*T above 2^31 - 1 tokens returns KDA_ERR_UNSUPPORTED.
  */
 kda_status kda_recurrent_verify(const void* q, const void* k, const void* v, const void* g,
                                 const void* beta_logits, const float* A_log, const float* dt_bias,

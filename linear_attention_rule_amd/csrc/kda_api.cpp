@@ -251,6 +251,9 @@ kda_status kda_recurrent_verify(const void* q, const void* k, const void* v, con
     return fail(KDA_ERR_INVALID_ARGUMENT, "bad sizes B=%d H=%d slots=%d", B, H, desc->num_slots);
   if (T < 1 || T > KDA_MAX_VERIFY_STEPS)
     return fail(KDA_ERR_UNSUPPORTED, "num_steps %d outside 1..%d", T, KDA_MAX_VERIFY_STEPS);
+  // The kernel numbers a row's tokens b*T + t in 32-bit integers.
+  if (static_cast<int64_t>(B) * T > INT32_MAX)
+    return fail(KDA_ERR_UNSUPPORTED, "batch %d x num_steps %d exceeds 2^31 - 1 tokens", B, T);
   if (kda_status s = check_lower_bound(lower_bound)) return s;
   if (!A_log || !dt_bias || !state_pool)
     return fail(KDA_ERR_INVALID_ARGUMENT, "A_log / dt_bias / state_pool is NULL");

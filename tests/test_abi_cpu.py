@@ -103,6 +103,8 @@ def test_verify_rejects_bad_arguments(lib):
     assert _verify(lib, _vdesc(D=96)) == UNSUPPORTED
     assert _verify(lib, _vdesc(T=0)) == UNSUPPORTED
     assert _verify(lib, _vdesc(T=65)) == UNSUPPORTED
+    assert _verify(lib, _vdesc(Bn=(1 << 26), T=64)) == UNSUPPORTED   # 2^32 tokens
+    assert b"exceeds" in lib.kda_last_error()
     assert _verify(lib, _vdesc(slots=0)) == INVALID
     assert _verify(lib, _vdesc(), lb=-7.0) == UNSUPPORTED
     # intermediate overlapping the pool
