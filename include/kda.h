@@ -162,6 +162,30 @@ kda_status kda_chunk_prefill_scan(const void* q, const void* k, const void* v, c
                                   const kda_prefill_desc* desc, void* stream);
 
 /*
+ * kda_chunk_prefill without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Arguments, results and checks are those of kda_chunk_prefill;
+ * the chunk records and segment states live in a fixed device array of
+ * KDA_NOALLOC_SCRATCH_BYTES inside libkda instead.
+ *  - Each GPU holds its own array, from the first call on that GPU until the process
+ *    ends.  The call itself allocates and frees nothing.
+ *  - Shapes whose kda_chunk_prefill_workspace_size exceeds KDA_NOALLOC_SCRATCH_BYTES
+ *    return KDA_ERR_UNSUPPORTED without enqueuing work (e.g. H = 16 heads fit up to
+ *    about 8K tokens per call).
+ *  - Every call on one GPU shares that GPU's array and overwrites it before reading
+ *    it; calls that overlap on one GPU (other streams, other threads) race and must
+ *    be serialised by the caller.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (128ll * 1024 * 1024)
+kda_status kda_chunk_prefill_noalloc(const void* q, const void* k, const void* v, const void* g,
+                                     const void* beta_logits, const float* A_log,
+                                     const float* dt_bias, float lower_bound,
+                                     const int32_t* cu_seqlens, const float* initial_state,
+                                     const int32_t* initial_state_idx, void* out,
+                                     float* final_state, const kda_prefill_desc* desc,
+                                     void* stream);
+
+/*
  * Fused multi-step verify (TensorRT-LLM PR #21179, fused-verify commit: the
  * fused_recurrent_kda role).  For each row b the state starts from
  * state_pool[state_idx[b]] (the pool is only read) and the T tokens of the row

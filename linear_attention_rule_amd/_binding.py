@@ -99,6 +99,9 @@ def load_library(path: str | None = None):
         fn.restype = ctypes.c_int
         fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, vp, sz,
                        ctypes.POINTER(PrefillDesc), vp]
+    lib.kda_chunk_prefill_noalloc.restype = ctypes.c_int
+    lib.kda_chunk_prefill_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp,
+                                              ctypes.POINTER(PrefillDesc), vp]
     lib.kda_recurrent_verify.restype = ctypes.c_int
     lib.kda_recurrent_verify.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp,
                                          ctypes.POINTER(VerifyDesc), vp]
@@ -194,15 +197,23 @@ def _out_index(out, out_token_index, tokens, H):
     return os_, int(out.shape[0]), _ptr(out_token_index)
 
 
+def noalloc_scratch_bytes() -> int:
+    """Size of the fixed per-device scratch behind chunk_prefill_noalloc (KDA_NOALLOC_SCRATCH_BYTES)."""
+    with open(HEADER_PATH) as f:
+        m = re.search(r"#define KDA_NOALLOC_SCRATCH_BYTES \((\d+)ll \* 1024 \* 1024\)", f.read())
+    return int(m.group(1)) << 20
+
+
 def chunk_prefill(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, cu_seqlens, *,
                   initial_state=None, initial_state_idx=None, out=None, final_state=None,
                   write_final_state=True, scale=None, workspace=None, check=False,
                   phase="both", out_token_index=None):
     """Varlen chunked KDA prefill.  Returns (out, final_state or None).
 
-    phase: "both" (kda_chunk_prefill), or "intra" / "scan" for the two halves of
-    the same call (kda_chunk_prefill_intra / kda_chunk_prefill_scan), which must
-    then be given the same workspace.
+    phase: "both" (kda_chunk_prefill), "intra" / "scan" for the two halves of the
+    same call (kda_chunk_prefill_intra / kda_chunk_prefill_scan), which must then be
+    given the same workspace, or "noalloc" (kda_chunk_prefill_noalloc: no workspace,
+    the library's fixed per-device scratch instead).
 
     out_token_index: optional int32 [T] on the device; token t's output goes to row
     out_token_index[t] of `out` (which must then be given: the layer buffer), rows
@@ -246,8 +257,16 @@ def chunk_prefill(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, cu_seqle
         final_state = torch.empty((N, H, HEAD_DIM, HEAD_DIM), dtype=torch.float32, device=dev)
     if final_state is not None:
         _f32("final_state", final_state, (N, H, HEAD_DIM, HEAD_DIM))
+    if phase not in ("both", "intra", "scan", "noalloc"):
+        raise ValueError(f"unknown phase {phase!r}")
     need = int(lib.kda_chunk_prefill_workspace_size(N, T, H, HEAD_DIM))
-    if workspace is None:
+    if phase == "noalloc":
+        if workspace is not None:
+            raise ValueError("phase='noalloc' takes no workspace")
+    elif workspace is None:
+        if phase != "both":
+            # The scan reads the records the intra phase left in this same buffer.
+            raise ValueError(f"phase={phase!r} needs the workspace shared by both phases")
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     if check:
         cu = cu_seqlens.cpu()
@@ -255,16 +274,31 @@ def chunk_prefill(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, cu_seqle
             raise ValueError("cu_seqlens must start at 0, be non-decreasing and end at T")
     desc = PrefillDesc(N, T, H, HEAD_DIM, float(scale) if scale else 0.0, rows,
                        qs, ks, vs, gs, bs, os_, oidx, out_rows)
-    fn = {"both": lib.kda_chunk_prefill, "intra": lib.kda_chunk_prefill_intra,
-          "scan": lib.kda_chunk_prefill_scan}[phase]
-    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta_logits), _ptr(A_log),
-                               _ptr(dt_bias), float(lower_bound), _ptr(cu_seqlens),
-                               _ptr(initial_state), _ptr(initial_state_idx), _ptr(out),
-                               _ptr(final_state), _ptr(workspace),
-                               workspace.numel() * workspace.element_size(), ctypes.byref(desc),
-                               _stream_handle(dev))
+    if phase == "noalloc":
+        st = lib.kda_chunk_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta_logits),
+                                           _ptr(A_log), _ptr(dt_bias), float(lower_bound),
+                                           _ptr(cu_seqlens), _ptr(initial_state),
+                                           _ptr(initial_state_idx), _ptr(out), _ptr(final_state),
+                                           ctypes.byref(desc), _stream_handle(dev))
+    else:
+        fn = {"both": lib.kda_chunk_prefill, "intra": lib.kda_chunk_prefill_intra,
+              "scan": lib.kda_chunk_prefill_scan}[phase]
+        st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta_logits), _ptr(A_log),
+                _ptr(dt_bias), float(lower_bound), _ptr(cu_seqlens), _ptr(initial_state),
+                _ptr(initial_state_idx), _ptr(out), _ptr(final_state), _ptr(workspace),
+                workspace.numel() * workspace.element_size(), ctypes.byref(desc),
+                _stream_handle(dev))
     _check(st)
     return out, final_state
+
+
+def chunk_prefill_noalloc(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, cu_seqlens,
+                          **kw):
+    """kda_chunk_prefill_noalloc: chunk_prefill with the library's fixed per-device scratch
+    in place of a workspace (no device allocation in the call itself, given `out` and
+    `final_state`).  Same arguments as chunk_prefill, without workspace and phase."""
+    return chunk_prefill(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, cu_seqlens,
+                         phase="noalloc", **kw)
 
 
 def recurrent_verify(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, state_pool, state_idx,

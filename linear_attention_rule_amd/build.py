@@ -17,7 +17,7 @@ LIB = os.path.join(HERE, "libkda.so")
 ARCH = "gfx950"
 
 SOURCES = ["kda_api.cpp", "kda_verify.hip", "kda_commit.hip", "kda_norm.hip", "kda_conv.hip",
-           "kda_prefill_intra.hip", "kda_prefill_scan.hip"]
+           "kda_prefill_intra.hip", "kda_prefill_scan.hip", "kda_scratch.hip"]
 
 # Per-source additions.  The intra kernel is a chain of short LDS / MFMA phases; the
 # ILP-first scheduler batches each phase's LDS reads ahead of their uses (measured on
@@ -50,22 +50,28 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source and link libkda.so; returns its path."""
+    """Compile every source (in parallel) and link libkda.so; returns its path."""
+    from concurrent.futures import ThreadPoolExecutor
+
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = []
     cc = hipcc()
-    for src in SOURCES:
+
+    def compile_one(src):
         obj = os.path.join(objdir, src + ".o")
-        xflag = ["-x", "hip"] if src.endswith(".hip") else ["-x", "hip"]
-        cmd = [cc, *HIP_FLAGS, *EXTRA_FLAGS.get(src, []), *xflag, "-c", os.path.join(CSRC, src),
-               "-o", obj]
+        # The C ABI source includes HIP headers and launches kernels: hip mode for all.
+        cmd = [cc, *HIP_FLAGS, *EXTRA_FLAGS.get(src, []), "-x", "hip", "-c",
+               os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
-        objs.append(obj)
+        return obj
+
+    jobs = max(1, min(len(SOURCES), os.cpu_count() or 1, 8))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:

@@ -12,6 +12,9 @@
 #include "../../include/kda.h"
 #include "kda_internal.h"
 
+static_assert(KDA_NOALLOC_SCRATCH_BYTES == kda::NOALLOC_SCRATCH_BYTES,
+              "kda.h and kda_internal.h disagree on the fixed scratch size");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -126,7 +129,7 @@ kda_status prefill_phases(const void* q, const void* k, const void* v, const voi
                           const float* initial_state, const int32_t* initial_state_idx,
                           void* out, float* final_state, void* workspace,
                           size_t workspace_bytes, const kda_prefill_desc* desc, void* stream,
-                          int phases) {
+                          int phases, bool use_scratch = false) {
   if (!desc) return fail(KDA_ERR_INVALID_ARGUMENT, "desc is NULL");
   const int N = desc->num_seqs, T = desc->total_tokens, H = desc->num_heads;
   if (desc->head_dim != KDA_HEAD_DIM)
@@ -174,6 +177,22 @@ kda_status prefill_phases(const void* q, const void* k, const void* v, const voi
   if ((initial_state && !aligned16(initial_state)) || (final_state && !aligned16(final_state)))
     return fail(KDA_ERR_INVALID_ARGUMENT, "state buffers must be 16-byte aligned");
   const size_t need = kda_chunk_prefill_workspace_size(N, T, H, KDA_HEAD_DIM);
+  if (use_scratch) {
+    // kda_chunk_prefill_noalloc: the same bytes from the library's fixed per-device array,
+    // looked up only once every other check has passed.
+    if (need > static_cast<size_t>(KDA_NOALLOC_SCRATCH_BYTES))
+      return fail(KDA_ERR_UNSUPPORTED,
+                  "N=%d T_total=%d H=%d needs %zu bytes of scratch; the fixed scratch holds %zu",
+                  N, T, H, need, static_cast<size_t>(KDA_NOALLOC_SCRATCH_BYTES));
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (need > 0 && N > 0) {
+      const hipError_t e = kda::noalloc_scratch(&workspace);
+      if (e != hipSuccess)
+        return fail(KDA_ERR_HIP, "scratch lookup failed: %s", hipGetErrorString(e));
+      workspace_bytes = need;
+    }
+  }
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need,
                 workspace ? workspace_bytes : static_cast<size_t>(0));
@@ -236,6 +255,18 @@ kda_status kda_chunk_prefill_intra(KDA_PREFILL_ARGS) {
 }
 kda_status kda_chunk_prefill_scan(KDA_PREFILL_ARGS) {
   return prefill_phases(KDA_PREFILL_FWD, kda::PHASE_SCAN);
+}
+
+kda_status kda_chunk_prefill_noalloc(const void* q, const void* k, const void* v, const void* g,
+                                     const void* beta_logits, const float* A_log,
+                                     const float* dt_bias, float lower_bound,
+                                     const int32_t* cu_seqlens, const float* initial_state,
+                                     const int32_t* initial_state_idx, void* out,
+                                     float* final_state, const kda_prefill_desc* desc,
+                                     void* stream) {
+  return prefill_phases(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, cu_seqlens,
+                        initial_state, initial_state_idx, out, final_state, nullptr, 0, desc,
+                        stream, kda::PHASE_INTRA | kda::PHASE_SCAN, /*use_scratch=*/true);
 }
 
 kda_status kda_recurrent_verify(const void* q, const void* k, const void* v, const void* g,

@@ -172,4 +172,10 @@ inline int64_t prefill_segment_bytes(int N, int H) {
   return pairs <= SEG_MAX_PAIRS ? pairs * SEG_SLOTS * D * D * 4 : 0;
 }
 
+// Fixed per-device scratch of the allocation-free prefill (kda_scratch.hip); equal to
+// KDA_NOALLOC_SCRATCH_BYTES in include/kda.h.
+constexpr int64_t NOALLOC_SCRATCH_BYTES = int64_t{128} << 20;
+// Device address of this device's scratch array (looked up once per device).
+hipError_t noalloc_scratch(void** out);
+
 }  // namespace kda

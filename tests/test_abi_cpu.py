@@ -243,3 +243,37 @@ def test_conv_prefill_launch_size_limit(lib):
     limit_T = 16 * ((2**24 - 1) // 3 - 1)                  # (T/16 + 1) * 3 <= 2^24 - 1
     assert pre(limit_T, 6144) not in (INVALID, UNSUPPORTED)
     assert pre(limit_T + 16 * 2, 6144) == UNSUPPORTED
+
+
+def test_noalloc_prefill_rejects_shapes_beyond_its_scratch(lib):
+    f = _fake
+    limit = B.noalloc_scratch_bytes()
+    assert limit == 128 << 20
+
+    def call(desc):
+        # fake buffers 2^32 bytes apart, so no two of them overlap at these sizes
+        g = lambda n: ctypes.c_void_p(n << 32)
+        return lib.kda_chunk_prefill_noalloc(g(1), g(2), g(3), g(4), g(5), g(6), g(7), -5.0, g(8),
+                                             None, None, g(9), g(10), ctypes.byref(desc), None)
+
+    # 4 x 8192 tokens at 16 heads: (512 + 4) x 16 records of 61 KiB, far beyond the scratch.
+    assert lib.kda_chunk_prefill_workspace_size(4, 32768, 16, 128) > limit
+    assert call(_pdesc(N=4, T=32768, H=16)) == UNSUPPORTED
+    assert b"fixed scratch" in lib.kda_last_error()
+    assert lib.kda_chunk_prefill_noalloc(f(1), f(2), f(3), f(4), f(5), f(6), f(7), -5.0, f(8),
+                                         None, None, f(9), f(10), None, None) == INVALID
+    assert call(_pdesc(D=64)) == UNSUPPORTED
+    # Inside the limit the checks are kda_chunk_prefill's, all made before the scratch is
+    # looked up (no GPU in this process, so a lookup would fail with KDA_ERR_HIP).
+    assert lib.kda_chunk_prefill_workspace_size(1, 64, 2, 128) <= limit
+    d = _pdesc(N=1, T=64, H=2)
+    assert lib.kda_chunk_prefill_noalloc(f(1), f(2), f(3), f(4), f(5), f(6), f(7), -7.0, f(8),
+                                         None, None, f(9), f(10), ctypes.byref(d), None) \
+        == UNSUPPORTED
+    assert lib.kda_chunk_prefill_noalloc(None, f(2), f(3), f(4), f(5), f(6), f(7), -5.0, f(8),
+                                         None, None, f(9), f(10), ctypes.byref(d), None) \
+        == INVALID
+    d.q_token_stride = 100
+    assert lib.kda_chunk_prefill_noalloc(f(1), f(2), f(3), f(4), f(5), f(6), f(7), -5.0, f(8),
+                                         None, None, f(9), f(10), ctypes.byref(d), None) \
+        == INVALID
