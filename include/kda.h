@@ -31,8 +31,14 @@
  *    Device-side contents (cu_seqlens monotone with cu[0] = 0 and
  *    cu[N] == total_tokens, indices in range, finite inputs) are preconditions.
  *  - Results are deterministic run to run (no atomics).
- *  - fp16 is used for intermediate MFMA operands in prefill: values of v and
- *    of the state must stay below 2^14 in magnitude.
+ *  - Prefill feeds fp16 MFMA operands with v, the state and values a small
+ *    multiple of them (X = V - K_Gamma S and U = T X of the chunked form), so |v|
+ *    and |state| must stay below 2^14.  Within that range the largest operand stays
+ *    a few times below the fp16 maximum (65504); past it an operand can overflow,
+ *    and out and final_state then hold inf or NaN while the call still returns
+ *    KDA_OK (device contents are never checked).  The Python binding's check=True
+ *    rejects |v| or |initial_state| >= 2^14.  Verify computes in fp32 throughout
+ *    and has no such limit.
  */
 #ifndef KDA_H
 #define KDA_H

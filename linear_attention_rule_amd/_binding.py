@@ -20,6 +20,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkda.so")
 HEADER_PATH = os.path.join(os.path.dirname(HERE), "include", "kda.h")
 HEAD_DIM = 128
+# Magnitude bound on v and the prefill state (fp16 MFMA operands in the scan).
+FP16_RANGE_LIMIT = 2.0 ** 14
 
 KDA_OK = 0
 STATUS_NAMES = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
@@ -272,6 +274,14 @@ def chunk_prefill(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, cu_seqle
         cu = cu_seqlens.cpu()
         if int(cu[0]) != 0 or int(cu[-1]) != T or bool((cu[1:] < cu[:-1]).any()):
             raise ValueError("cu_seqlens must start at 0, be non-decreasing and end at T")
+        # The scan's fp16 MFMA operands hold v, the state and values a small multiple of
+        # them: inputs at or past 2^14 may overflow fp16 (FP16_RANGE_LIMIT in kda.h).
+        if T > 0 and not bool((v.abs() < FP16_RANGE_LIMIT).all()):
+            raise ValueError(f"|v| must stay below {FP16_RANGE_LIMIT:g} (fp16 scan operands)")
+        if initial_state is not None and initial_state.numel() and \
+                not bool((initial_state.abs() < FP16_RANGE_LIMIT).all()):
+            raise ValueError(f"|initial_state| must stay below {FP16_RANGE_LIMIT:g} "
+                             "(fp16 scan operands)")
     desc = PrefillDesc(N, T, H, HEAD_DIM, float(scale) if scale else 0.0, rows,
                        qs, ks, vs, gs, bs, os_, oidx, out_rows)
     if phase == "noalloc":

@@ -176,6 +176,40 @@ kda_status prefill_phases(const void* q, const void* k, const void* v, const voi
   }
   if ((initial_state && !aligned16(initial_state)) || (final_state && !aligned16(final_state)))
     return fail(KDA_ERR_INVALID_ARGUMENT, "state buffers must be 16-byte aligned");
+  // The intra kernel reads dt_bias rows as 16-byte vectors.
+  if (!aligned16(dt_bias) || (reinterpret_cast<uintptr_t>(A_log) & 3u))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "dt_bias must be 16-byte and A_log 4-byte aligned");
+  {
+    // States: the final states are written while other workgroups still read the
+    // inputs and the start states, so they may share no byte with them, except that
+    // final_state may be initial_state itself when both are indexed by sequence (each
+    // workgroup reads its start columns before it writes them).
+    const int64_t state_elems = static_cast<int64_t>(KDA_HEAD_DIM) * KDA_HEAD_DIM;
+    const Span s_init = initial_state
+                            ? span_of(initial_state, desc->num_state_rows, H * state_elems,
+                                      H * state_elems, 4)
+                            : Span{0, 0};
+    const Span s_fin = final_state ? span_of(final_state, N, H * state_elems, H * state_elems, 4)
+                                   : Span{0, 0};
+    if (final_state && initial_state && overlaps(s_fin, s_init) &&
+        !(final_state == initial_state && !initial_state_idx))
+      return fail(KDA_ERR_INVALID_ARGUMENT,
+                  "final_state overlaps initial_state (only final_state == initial_state "
+                  "without initial_state_idx is allowed)");
+    if (T > 0) {
+      const void* ins[5] = {q, k, v, g, beta_logits};
+      const int64_t sts[5] = {qs, ks, vs, gs, bs};
+      const int64_t widths[5] = {HD, HD, HD, HD, H};
+      const Span so = span_of(out, orows, os, HD, 2);
+      for (int i = 0; i < 5; ++i)
+        if (final_state && overlaps(s_fin, span_of(ins[i], T, sts[i], widths[i], 2)))
+          return fail(KDA_ERR_INVALID_ARGUMENT, "final_state overlaps an input");
+      if (final_state && overlaps(s_fin, so))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "final_state overlaps out");
+      if (initial_state && overlaps(s_init, so))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "out overlaps initial_state");
+    }
+  }
   const size_t need = kda_chunk_prefill_workspace_size(N, T, H, KDA_HEAD_DIM);
   if (use_scratch) {
     // kda_chunk_prefill_noalloc: the same bytes from the library's fixed per-device array,
@@ -324,6 +358,13 @@ kda_status kda_recurrent_verify(const void* q, const void* k, const void* v, con
       return fail(KDA_ERR_INVALID_ARGUMENT, "out overlaps an input");
   if (overlaps(so, s_int) || overlaps(so, s_pool))
     return fail(KDA_ERR_INVALID_ARGUMENT, "out overlaps a state buffer");
+  if (overlaps(so, span_of(beta_logits, BT, bs, H, 2)))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "out overlaps beta_logits");
+  for (int i = 0; i < 4; ++i)
+    if (overlaps(s_int, span_of(ins[i], BT, sts[i], HD, 2)))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "intermediate_state overlaps an input");
+  if (overlaps(s_int, span_of(beta_logits, BT, bs, H, 2)))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "intermediate_state overlaps beta_logits");
 
   kda::VerifyParams p{};
   p.q = static_cast<const uint16_t*>(q);

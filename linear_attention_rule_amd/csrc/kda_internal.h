@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 #include <stdint.h>
 
 namespace kda {
@@ -39,6 +40,38 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 __device__ __forceinline__ float sigmoid_f32(float x) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * LOG2E));
 }
+
+// ---------------------------------------------------------------- per-device host state
+// One-time set-up per device (function attributes, device properties), kept for the
+// life of the process so that no call pays a runtime query after the first one on a
+// device.  Only successful results are kept.
+constexpr int KDA_MAX_DEVICES = 64;
+struct PerDeviceOnce {
+  std::mutex mu;
+  bool done[KDA_MAX_DEVICES] = {};
+  int value[KDA_MAX_DEVICES] = {};
+  // Runs f(&value) for the current device unless it already succeeded there.
+  template <class F>
+  hipError_t run(F&& f, int* out = nullptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= KDA_MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!done[dev]) {
+      int v = 0;
+      e = f(dev, &v);
+      if (e != hipSuccess) return e;
+      value[dev] = v;
+      done[dev] = true;
+    }
+    if (out) *out = value[dev];
+    return hipSuccess;
+  }
+};
+
+// Compute units of the current device (looked up once per device).
+hipError_t current_device_cus(int* cus);
 
 // ---------------------------------------------------------------- launch parameters
 struct VerifyParams {

@@ -767,9 +767,8 @@ hipError_t launch_prefill(const PrefillParams& p_in, int phases, hipStream_t s) 
     if (e != hipSuccess) return e;
   }
   if (!(phases & PHASE_SCAN)) return hipSuccess;
-  int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  int cus = 0;
+  hipError_t e = current_device_cus(&cus);
   if (e != hipSuccess) return e;
   PrefillParams p = p_in;
   const int64_t pairs = static_cast<int64_t>(p.N) * p.H;

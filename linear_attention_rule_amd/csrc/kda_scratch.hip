@@ -1,4 +1,7 @@
-// Fixed device scratch for kda_chunk_prefill_noalloc: the chunk records and segment
+// Per-device host state: the fixed device scratch of kda_chunk_prefill_noalloc and the
+// device properties the launchers query once per device.
+//
+// The scratch: the chunk records and segment
 // states that kda_chunk_prefill keeps in a caller workspace live here instead, for
 // callers that cannot allocate (code under stream capture, tight serving loops).
 //
@@ -39,6 +42,15 @@ hipError_t noalloc_scratch(void** out) {
   }
   *out = g_scratch_ptr[dev];
   return hipSuccess;
+}
+
+hipError_t current_device_cus(int* cus) {
+  static PerDeviceOnce once;
+  return once.run(
+      [](int dev, int* v) {
+        return hipDeviceGetAttribute(v, hipDeviceAttributeMultiprocessorCount, dev);
+      },
+      cus);
 }
 
 }  // namespace kda

@@ -192,9 +192,14 @@ size_t verify_lds_bytes(int T) {
 template <int BV>
 hipError_t launch_verify_bv(const VerifyParams& p, hipStream_t s) {
   const size_t lds = verify_lds_bytes<BV>(p.T);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&verify_kernel<BV>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     static_cast<int>(verify_lds_bytes<BV>(KDA_MAX_STEPS_INTERNAL)));
+  // The LDS limit for the largest step count is set once per device, not per call
+  // (verify at batch 1 is latency-bound).
+  static PerDeviceOnce attr_once;
+  hipError_t e = attr_once.run([](int, int*) {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(&verify_kernel<BV>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                               static_cast<int>(verify_lds_bytes<BV>(KDA_MAX_STEPS_INTERNAL)));
+  });
   if (e != hipSuccess) return e;
   const dim3 grid(static_cast<unsigned>(p.B) * p.H * (D / BV));
   hipLaunchKernelGGL(verify_kernel<BV>, grid, dim3(256), lds, s, p);

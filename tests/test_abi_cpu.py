@@ -277,3 +277,44 @@ def test_noalloc_prefill_rejects_shapes_beyond_its_scratch(lib):
     assert lib.kda_chunk_prefill_noalloc(f(1), f(2), f(3), f(4), f(5), f(6), f(7), -5.0, f(8),
                                          None, None, f(9), f(10), ctypes.byref(d), None) \
         == INVALID
+
+
+def test_prefill_alignment_and_state_overlap_checks(lib):
+    g = lambda n: ctypes.c_void_p(n << 32)      # fake buffers 4 GiB apart
+    d = _pdesc(N=2, T=128, H=2)
+    d.num_state_rows = 2
+
+    def call(dt=g(7), A=g(6), init=None, idx=None, out=g(9), fin=g(10), q=g(1), ws_bytes=1 << 40):
+        return lib.kda_chunk_prefill(q, g(2), g(3), g(4), g(5), A, dt, -5.0, g(8), init, idx,
+                                     out, fin, g(11), ws_bytes, ctypes.byref(d), None)
+
+    # dt_bias is read as 16-byte vectors, A_log as words
+    assert call(dt=ctypes.c_void_p((7 << 32) + 8)) == INVALID
+    assert b"dt_bias" in lib.kda_last_error()
+    assert call(A=ctypes.c_void_p((6 << 32) + 2)) == INVALID
+    # final_state sharing bytes with an input, with out, or partly with initial_state
+    assert call(fin=ctypes.c_void_p((1 << 32) + 4096)) == INVALID
+    assert b"final_state overlaps an input" in lib.kda_last_error()
+    assert call(fin=ctypes.c_void_p((5 << 32) + 16)) == INVALID      # beta logits
+    assert call(fin=ctypes.c_void_p((9 << 32) - 65536)) == INVALID   # runs into out
+    assert call(init=g(12), fin=ctypes.c_void_p((12 << 32) + 65536)) == INVALID
+    assert b"initial_state" in lib.kda_last_error()
+    # out over the start states
+    assert call(init=g(12), out=ctypes.c_void_p((12 << 32) + 1024)) == INVALID
+    # in place over the start states is allowed only when indexed by sequence
+    assert call(init=g(12), fin=g(12), idx=g(13)) == INVALID
+    assert call(init=g(12), fin=g(12), ws_bytes=100) == WS_SMALL     # every other check passed
+
+
+def test_verify_rejects_out_over_beta_and_states_over_inputs(lib):
+    f = _fake
+    d = _vdesc(Bn=2, T=8, H=2)
+    # beta logits [16, 2] bf16 at f(5); out starting inside them
+    st = lib.kda_recurrent_verify(f(1), f(2), f(3), f(4), f(5), f(6), f(7), -5.0, f(20), f(9),
+                                  f(40), ctypes.c_void_p(0x50000 + 32), ctypes.byref(d), None)
+    assert st == INVALID and b"beta_logits" in lib.kda_last_error()
+    # per-step states written over q
+    st = lib.kda_recurrent_verify(ctypes.c_void_p(0x400000 + 4096), f(2), f(3), f(4), f(5), f(6),
+                                  f(7), -5.0, f(20), f(9), ctypes.c_void_p(0x400000), f(50),
+                                  ctypes.byref(d), None)
+    assert st == INVALID and b"intermediate_state overlaps" in lib.kda_last_error()

@@ -3,9 +3,9 @@
 All calls go through the C ABI (ctypes binding) on seeded inputs from
 linear_attention_rule_amd.workloads.  Small cases are compared element by
 element in full.  At the full workload sizes the GPU runs the real launch (all
-heads, all sequences) and the oracle recomputes a sample of (sequence, head)
-pairs over their whole length: heads are independent, so each sampled pair is
-an exact sub-problem of the same call.
+heads, all sequences) and the oracle recomputes every (sequence, head) pair over
+its whole length (about 30 s of one host core for the three workloads); a sampled
+variant recomputes a few pairs only, as a fast first check.
 """
 
 import numpy as np
@@ -306,6 +306,45 @@ def test_prefill_matches_verify_on_block_sequences():
     TOL.assert_state_ok(iv[:, -1], i_ref[:, -1])
 
 
+# ---------------------------------------------------------------- fp16 operand range
+
+def test_prefill_large_values_near_2_13():
+    """v and the start states scaled by a power of two to |v| in [2^12, 2^13): the fp16
+    scan operands (S, X = V - K_Gamma S, U = T'X) grow with them and must stay in range;
+    the relative bar is unchanged.  check=True accepts the call."""
+    case = W.PrefillCase("large_v", [2048, 700, 64], 4, init="per_seq", seed=3301)
+    data = W.make_prefill(case)
+    c = 2.0 ** np.floor(np.log2(2.0 ** 13 / float(data["v"].float().abs().max())))
+    data["v"] = (data["v"].float() * c).to(torch.bfloat16)             # exact: power of two
+    data["initial_state"] = data["initial_state"] * c
+    vmax = float(data["v"].float().abs().max())
+    print(f"case {case.name} max|v| {vmax:.0f}", flush=True)
+    assert 2.0 ** 12 <= vmax < 2.0 ** 13
+    d = _dev(data)
+    out, final = _call(d, check=True)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out.float()).all()) and bool(torch.isfinite(final).all())
+    _compare(data, out, final)
+
+
+def test_prefill_check_rejects_values_past_the_fp16_range():
+    case = W.PrefillCase("too_large_v", [100], 2, init="per_seq", seed=3302)
+    data = W.make_prefill(case)
+    d = _dev(data)
+    big = d["v"].clone()
+    big[3, 1, 7] = 2.0 ** 14
+    with pytest.raises(ValueError, match="v"):
+        chunk_prefill(d["q"], d["k"], big, d["g"], d["beta_logits"], d["A_log"], d["dt_bias"],
+                      d["lower_bound"], d["cu_seqlens"], initial_state=d["initial_state"],
+                      check=True)
+    init = d["initial_state"].clone()
+    init[0, 0, 5, 5] = -2.0 ** 14
+    with pytest.raises(ValueError, match="initial_state"):
+        chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta_logits"], d["A_log"],
+                      d["dt_bias"], d["lower_bound"], d["cu_seqlens"], initial_state=init,
+                      check=True)
+
+
 # ---------------------------------------------------------------- full workload sizes (sampled heads)
 
 FULL = [
@@ -329,6 +368,37 @@ def test_prefill_full_size_sampled(case, heads, seqs):
     if out is not None:
         assert o.data_ptr() == out.data_ptr()
     _compare(data, o, fin, heads=heads, seqs=seqs)
+
+
+@pytest.mark.parametrize("case", [c[0] for c in FULL], ids=[c[0].name for c in FULL])
+def test_prefill_full_size_every_pair(case):
+    """The launch the benchmark times, compared with the oracle on every (sequence, head)
+    pair: each pair's outputs against that pair's RMS and each pair's final state on its
+    own.  This covers every work unit of the scan's workgroup maps (value slices, XCD
+    interleave, segments)."""
+    print(f"case {case.name} seed {case.seed}: GPU call", flush=True)
+    data = W.make_prefill(case)
+    d = _dev(data)
+    out = None
+    if case.init == "pool":
+        out = torch.empty((d["q"].shape[0], d["q"].shape[1], 128), dtype=torch.bfloat16, device="cuda")
+    o, fin = _call(d, out=out) if out is not None else _call(d)
+    torch.cuda.synchronize()
+    o_gpu = o.cpu()
+    f_gpu = fin.cpu()
+    del d, o, fin
+    print("  oracle over every pair", flush=True)
+    o_ref, f_ref, _ = _oracle(data)
+    cu = data["cu_seqlens"].numpy().astype(np.int64)
+    N, H = len(cu) - 1, data["q"].shape[1]
+    worst_e, worst_r = 0.0, 0.0
+    for n in range(N):
+        for h in range(H):
+            e = TOL.assert_output_ok(o_gpu[cu[n]:cu[n + 1], h], o_ref[cu[n]:cu[n + 1], h])
+            r = TOL.assert_state_ok(f_gpu[n, h], f_ref[n, h])
+            worst_e, worst_r = max(worst_e, e["excess_over_rms"]), max(worst_r, r)
+    print(f"  {N * H} pairs: worst output excess/RMS {worst_e:.2e}, worst state rel L2 "
+          f"{worst_r:.2e}", flush=True)
 
 
 # ---------------------------------------------------------------- segment-parallel scan
