@@ -1,22 +1,26 @@
 """KDA prefill + verify benchmark on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--iters N]
 
 One step is one pass of the whole hot path over one batch of synthetic input:
-  * varlen chunked prefill of 4 sequences x 8192 tokens, H = 16, d = 128
-    (zero start state, fp32 final states): the intra-chunk kernel then the
-    state-scan kernel (kda_chunk_prefill_intra + kda_chunk_prefill_scan, which
-    together are exactly kda_chunk_prefill);
+  * varlen chunked prefill of 4 sequences x 8192 tokens, H = 16, d = 128 (zero
+    start state, fp32 final states): one kda_chunk_prefill call (the intra-chunk
+    kernel, then the state-scan kernel);
   * fused verify of 64 rows x 8 draft tokens, H = 16, states gathered from a
     256-slot fp32 pool, per-step fp32 states written (kda_recurrent_verify).
-Inputs are resident in HBM before timing starts.  Each kernel is bracketed by
-HIP events on the stream it is launched on (torch's current stream, which the
-binding hands to libkda).  Prints ONE JSON line on stdout; progress goes to stderr.
+Inputs are resident in HBM before timing starts.  Each call is bracketed by HIP
+events on the stream it is launched on (torch's current stream, which the
+binding hands to libkda); per-layer figures are medians.  Prints ONE JSON line
+on stdout; progress goes to stderr.
 
-`value` is prefill tokens/s at 4x8192 (the headline shape); prefill and verify
-microseconds per layer are reported beside it.  The oracle (fp64 CPU token
-loop) is timed on a bounded sample of the same prefill workload as
-`cpu_baseline`.
+`value` is prefill tokens/s at 4x8192 (the headline shape), and `roofline` is
+that call's: its algorithmic bytes (1282 B per token-head plus the final states)
+over the call's median time.  `configs` repeats the measurement per workload --
+8 x 2048 with start states, 4 x 8192, 1 x 16384 with a gathered start state and
+the verify -- as medians of at least 50 calls, warm and cold (1 GiB overwritten,
+or read, before each call), with each prefill's two kernels also timed alone.
+The oracle (fp64 CPU token loop) is timed on a bounded sample of the 4 x 8192
+workload as `cpu_baseline`.
 """
 
 from __future__ import annotations
@@ -146,8 +150,7 @@ def stored_traffic(kernel, workload):
 
 MAIN_WORKLOAD = f"prefill {W.LONG.name} + verify {W.VERIFY.name}"
 EXTRAS_WORKLOAD = (f"commit after {W.VERIFY.name} + conv {W.CONV_PREFILL.name} / "
-                   f"{W.CONV_UPDATE.name} + gated norm {W.NORM.name} + segmented prefill "
-                   f"{W.SINGLE_LONG.name} + mixed step {W.MIXED.name}")
+                   f"{W.CONV_UPDATE.name} + gated norm {W.NORM.name} + mixed step {W.MIXED.name}")
 
 
 N_XCD = 8           # MI355X: XCDs (GRBM_GUI_ACTIVE is read once per XCD)
@@ -375,7 +378,9 @@ def verify_latency_b1(iters):
                          vd["dt_bias"], vd["lower_bound"], vd["state_pool"], vd["state_idx"], Tv,
                          intermediate=inter, out=out, scale=vd["scale"])
 
-    res = {"workload": case.name, "us_plain_launch": round(time_calls(call, 10 * iters) * 1e6, 2)}
+    res = {"workload": case.name, "how": "mean over back-to-back calls (plain launches, and "
+           "replays of a graph of 20 calls)",
+           "us_plain_launch": round(time_calls(call, 10 * iters) * 1e6, 2)}
     call()
     torch.cuda.synchronize()
     ref = (out.clone(), inter.clone())
@@ -407,7 +412,8 @@ def verify_latency_b1(iters):
 
 
 def bench_next_rows(iters):
-    """The rows after the hot path: the rollback commit at the verify size, and one mixed
+    """The rows after the hot path (medians of `iters` calls): the rollback commit at the
+    verify size, the short conv (prefill and update), the gated output norm, and one mixed
     speculative step (prefill segment and spec rows scattered into one layer output)."""
     vcase = W.VERIFY
     B, Tv, H = vcase.batch, vcase.steps, vcase.heads
@@ -416,7 +422,7 @@ def bench_next_rows(iters):
     pool = torch.zeros((vcase.pool_slots, H, D, D), dtype=torch.float32, device="cuda")
     idx = torch.from_numpy(rng.permutation(vcase.pool_slots)[:B].astype(np.int32)).cuda()
     nacc = torch.from_numpy(rng.integers(1, Tv + 1, size=B).astype(np.int32)).cuda()
-    t_commit = time_calls(lambda: commit_accepted(inter, idx, nacc, pool), iters)
+    t_commit = median_call_us(lambda: commit_accepted(inter, idx, nacc, pool), iters) * 1e-6
     commit_bytes = B * H * 2 * STATE_BYTES + 2 * B * 4
     del inter, pool
 
@@ -440,28 +446,9 @@ def bench_next_rows(iters):
                          spec["state_idx"], Ts, intermediate=sinter, out=core, scale=spec["scale"],
                          out_token_index=sp_idx)
 
-    t_mixed = time_calls(mixed, iters)
+    t_mixed = median_call_us(mixed, iters) * 1e-6
     del core, ws, fin, sinter
 
-    # One long sequence with a gathered start state: few (sequence, head) pairs, so the
-    # scan runs segment-parallel (state maps per segment, combine, then the segments).
-    sc = W.SINGLE_LONG
-    sd = to_dev(W.make_prefill(sc))
-    Ts1, Hs1 = sd["q"].shape[0], sd["q"].shape[1]
-    s_ws = torch.empty(prefill_workspace_bytes(1, Ts1, Hs1), dtype=torch.uint8, device="cuda")
-    s_out = torch.empty((Ts1, Hs1, D), dtype=torch.bfloat16, device="cuda")
-    s_fin = torch.empty((1, Hs1, D, D), dtype=torch.float32, device="cuda")
-
-    def single(phase):
-        chunk_prefill(sd["q"], sd["k"], sd["v"], sd["g"], sd["beta_logits"], sd["A_log"],
-                      sd["dt_bias"], sd["lower_bound"], sd["cu_seqlens"],
-                      initial_state=sd["initial_state"], initial_state_idx=sd["initial_state_idx"],
-                      out=s_out, final_state=s_fin, workspace=s_ws, scale=sd["scale"], phase=phase)
-
-    t_s_intra = time_calls(lambda: single("intra"), iters)
-    t_s_scan = time_calls(lambda: single("scan"), iters)
-    s_bytes = Ts1 * Hs1 * BYTES_PER_TOKEN_HEAD + 2 * Hs1 * STATE_BYTES
-    t_single = t_s_intra + t_s_scan
     tokens = Tp + Bs * Ts
     mixed_bytes = (tokens * Hm * BYTES_PER_TOKEN_HEAD + Np * Hm * STATE_BYTES
                    + Bs * Hm * STATE_BYTES * (1 + Ts))
@@ -469,7 +456,7 @@ def bench_next_rows(iters):
     nx, ng, nw = nd["x"].cuda(), nd["gate"].cuda(), nd["weight"].cuda()
     ny = torch.empty_like(nx)
     nr = torch.empty(nx.shape[:2], dtype=torch.float32, device="cuda")
-    t_norm = time_calls(lambda: gated_rmsnorm(nx, ng, nw, nd["eps"], out=ny, rstd=nr), iters)
+    t_norm = median_call_us(lambda: gated_rmsnorm(nx, ng, nw, nd["eps"], out=ny, rstd=nr), iters) * 1e-6
     norm_rows = nx.shape[0] * nx.shape[1]
     norm_bytes = norm_rows * (3 * 2 * D + 4)
     rl_norm = roofline(norm_bytes, 0, t_norm)
@@ -481,8 +468,8 @@ def bench_next_rows(iters):
     cx, cw, cb = cp["x"].cuda(), cp["weight"].cuda(), cp["bias"].cuda()
     cst, cidx, ccu = cp["state"].cuda(), cp["state_idx"].cuda(), cp["cu_seqlens"].cuda()
     cy = torch.empty_like(cx)
-    t_convp = time_calls(lambda: causal_conv1d_prefill(cx, cw, cb, ccu, conv_state=cst,
-                                                       state_idx=cidx, out=cy), iters)
+    t_convp = median_call_us(lambda: causal_conv1d_prefill(cx, cw, cb, ccu, conv_state=cst,
+                                                           state_idx=cidx, out=cy), iters) * 1e-6
     Tc, Cc = cx.shape
     Wc = W.CONV_PREFILL.width
     Nc = ccu.numel() - 1
@@ -494,8 +481,8 @@ def bench_next_rows(iters):
     Bu, Tu = W.CONV_UPDATE.batch, W.CONV_UPDATE.steps
     uy = torch.empty_like(ux)
     uint = torch.empty((Bu, Tu, Wc - 1, Cc), dtype=torch.bfloat16, device="cuda")
-    t_convu = time_calls(lambda: causal_conv1d_update(ux, uw, ub, upool, uidx, Tu,
-                                                      intermediate=uint, out=uy), iters)
+    t_convu = median_call_us(lambda: causal_conv1d_update(ux, uw, ub, upool, uidx, Tu,
+                                                          intermediate=uint, out=uy), iters) * 1e-6
     convu_bytes = (2 * Bu * Tu * Cc * 2 + Bu * (Wc - 1) * Cc * 2 + Bu * Tu * (Wc - 1) * Cc * 2
                    + Cc * (Wc + 1) * 2)
     del ux, uy, upool, uint
@@ -514,12 +501,6 @@ def bench_next_rows(iters):
                         "roofline": rl_convu, "algorithmic_bytes": convu_bytes},
         "gated_rmsnorm": {"workload": W.NORM.name, "us": round(t_norm * 1e6, 2),
                           "roofline": rl_norm, "algorithmic_bytes": norm_bytes},
-        "segmented_prefill": {"workload": sc.name, "us": round(t_single * 1e6, 2),
-                              "intra_us": round(t_s_intra * 1e6, 2),
-                              "scan_us": round(t_s_scan * 1e6, 2),
-                              "tokens_per_s": round(Ts1 / t_single, 1),
-                              "roofline": roofline(s_bytes, 0, t_single),
-                              "algorithmic_bytes": s_bytes},
         "mixed_step": {"workload": W.MIXED.name, "us": round(t_mixed * 1e6, 2),
                        "tokens_per_s": round(tokens / t_mixed, 1),
                        "roofline": roofline(mixed_bytes, 0, t_mixed),
@@ -527,11 +508,107 @@ def bench_next_rows(iters):
     }
 
 
+def median_call_us(fn, iters, warmup=3):
+    """Median microseconds over `iters` calls of fn, each bracketed by its own pair of HIP
+    events on torch's current stream (the stream libkda launches on)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    for e0, e1 in evs:
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    return float(np.median([e0.elapsed_time(e1) for e0, e1 in evs])) * 1e3
+
+
+def cold_call_us(fn, iters, flush, how):
+    """Median microseconds of fn with the caches emptied first: `how` = "write" overwrites
+    the 1 GiB buffer `flush` (the protocol's cold run: evicts L2 and the 256 MB memory-side
+    cache, leaving them full of dirty lines), "read" reads it (evicts without dirty lines);
+    the flush completes before the timed call starts."""
+    ts = []
+    for _ in range(iters):
+        if how == "write":
+            flush.fill_(1.0)
+        else:
+            flush.sum()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return float(np.median(ts)) * 1e3
+
+
+def prefill_alg(case, T, H, N, init_rows_read):
+    """Algorithmic bytes and MFMA flops of one prefill call: 1282 B and 139,264 flop per
+    token-head, plus each start state read and each final state written (64 KiB)."""
+    bytes_ = T * H * BYTES_PER_TOKEN_HEAD + (init_rows_read + N) * H * STATE_BYTES
+    return bytes_, T * H * FLOPS_PER_TOKEN_HEAD
+
+
+def config_line(name, us, tokens, bytes_, flops, cold=None, extra=None):
+    t = us * 1e-6
+    hbm = roofline(bytes_, 0, t)
+    line = {"workload": name, "us_per_layer": round(us, 2), "tokens_per_s": round(tokens / t, 1),
+            "algorithmic_bytes": bytes_, "hbm": hbm}
+    if flops:
+        line["mfma"] = roofline(0, flops, t, bound="mfma")
+        line["roofline_frac"] = round(max(bytes_ / (HBM_PEAK_GBS * 1e9),
+                                          flops / (MFMA_BF16_PEAK_TFS * 1e12)) / t, 4)
+    else:
+        line["roofline_frac"] = hbm["frac"]
+    if cold:
+        line["cold_us"] = {k: round(v, 2) for k, v in cold.items()}
+        line["cold_hbm_frac"] = {k: round(bytes_ / (v * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                                 for k, v in cold.items()}
+    if extra:
+        line.update(extra)
+    return line
+
+
+class PrefillRun:
+    """Device inputs and caller buffers of one prefill workload (out preallocated)."""
+
+    def __init__(self, case):
+        self.case = case
+        self.d = to_dev(W.make_prefill(case))
+        d = self.d
+        self.T, self.H = d["q"].shape[0], d["q"].shape[1]
+        self.N = d["cu_seqlens"].numel() - 1
+        self.ws = torch.empty(prefill_workspace_bytes(self.N, self.T, self.H), dtype=torch.uint8,
+                              device="cuda")
+        self.out = torch.empty((self.T, self.H, D), dtype=torch.bfloat16, device="cuda")
+        self.fin = torch.empty((self.N, self.H, D, D), dtype=torch.float32, device="cuda")
+        self.init_rows_read = 0 if d["initial_state"] is None else self.N
+
+    def __call__(self, phase="both"):
+        d = self.d
+        chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta_logits"], d["A_log"], d["dt_bias"],
+                      d["lower_bound"], d["cu_seqlens"], initial_state=d["initial_state"],
+                      initial_state_idx=d["initial_state_idx"], out=self.out,
+                      final_state=self.fin, workspace=self.ws, scale=d["scale"], phase=phase)
+
+    def alg(self):
+        return prefill_alg(self.case, self.T, self.H, self.N, self.init_rows_read)
+
+    def free(self):
+        del self.d, self.ws, self.out, self.fin
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--iters", type=int, default=50,
+                    help="calls per median in the per-configuration protocol (at least 50)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=8192,
                     help="tokens per sequence in the oracle's timed sample (8192: the whole "
@@ -542,9 +619,10 @@ def main():
                     help="summarize rocprofv3 CSV output into --summary-out and exit")
     ap.add_argument("--summary-out", default=None)
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the commit and mixed-step measurements")
+                    help="skip the per-configuration protocol and the next rows (the timed "
+                         "steps and the per-kernel split only: for profiling)")
     ap.add_argument("--extras-only", action="store_true",
-                    help="measure only the commit and the mixed step (one JSON line)")
+                    help="measure only the next rows (one JSON line)")
     args = ap.parse_args()
     if args.summarize:
         extras = args.extras_only
@@ -560,56 +638,45 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    iters = max(50, args.iters)
 
     if args.calib_copy:
         calibration_copies()
     if args.extras_only:
-        print(json.dumps({"next_rows": bench_next_rows(args.steps)}), flush=True)
+        print(json.dumps({"next_rows": bench_next_rows(iters)}), flush=True)
         return
 
-    pcase, vcase = W.LONG, W.VERIFY
-    log(f"generating {pcase.name} and {vcase.name}")
-    pd = to_dev(W.make_prefill(pcase))
+    vcase = W.VERIFY
+    log(f"generating {W.LONG.name} and {vcase.name}")
+    long = PrefillRun(W.LONG)
     vd = to_dev(W.make_verify(vcase))
-    T, H = pd["q"].shape[0], pd["q"].shape[1]
-    N = pd["cu_seqlens"].numel() - 1
-    ws = torch.empty(prefill_workspace_bytes(N, T, H), dtype=torch.uint8, device="cuda")
-    out = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
-    fin = torch.empty((N, H, D, D), dtype=torch.float32, device="cuda")
+    T, H, N = long.T, long.H, long.N
     B, Tv = vcase.batch, vcase.steps
     vout = torch.empty((B * Tv, H, D), dtype=torch.bfloat16, device="cuda")
     inter = torch.empty((B, Tv, H, D, D), dtype=torch.float32, device="cuda")
-
-    def prefill(phase):
-        chunk_prefill(pd["q"], pd["k"], pd["v"], pd["g"], pd["beta_logits"], pd["A_log"],
-                      pd["dt_bias"], pd["lower_bound"], pd["cu_seqlens"], out=out, final_state=fin,
-                      workspace=ws, scale=pd["scale"], phase=phase)
 
     def verify():
         recurrent_verify(vd["q"], vd["k"], vd["v"], vd["g"], vd["beta_logits"], vd["A_log"],
                          vd["dt_bias"], vd["lower_bound"], vd["state_pool"], vd["state_idx"], Tv,
                          intermediate=inter, out=vout, scale=vd["scale"])
 
+    # One step = one pass of the hot path: the whole prefill call (kda_chunk_prefill, both
+    # kernels) at 4 x 8192, then the verify call at 64 x 8; each call between its own events.
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        prefill("intra")
+        long()
         if ev is not None:
             ev[1].record()
-        prefill("scan")
-        if ev is not None:
-            ev[2].record()
         verify()
         if ev is not None:
-            ev[3].record()
-
+            ev[2].record()
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -619,71 +686,80 @@ def main():
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
-    t_intra = [e[0].elapsed_time(e[1]) * 1e-3 for e in evs]
-    t_scan = [e[1].elapsed_time(e[2]) * 1e-3 for e in evs]
-    t_ver = [e[2].elapsed_time(e[3]) * 1e-3 for e in evs]
-    s_intra, s_scan, s_ver = (float(np.mean(x)) for x in (t_intra, t_scan, t_ver))
-    s_prefill = s_intra + s_scan
-    log(f"intra {s_intra * 1e6:.1f} us  scan {s_scan * 1e6:.1f} us  verify {s_ver * 1e6:.1f} us")
+    s_prefill = float(np.median([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
+    s_ver = float(np.median([e[1].elapsed_time(e[2]) for e in evs])) * 1e-3
+    log(f"timed steps: prefill call {s_prefill * 1e6:.1f} us  verify {s_ver * 1e6:.1f} us "
+        f"(medians of {args.steps})")
 
-    # Cold-cache pass: overwrite 1 GiB between iterations (outside the events).
-    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-    cold_p, cold_v = [], []
-    for _ in range(5):
-        flush.fill_(1.0)
-        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-        e0.record()
-        prefill("both")
-        e1.record()
-        flush.fill_(2.0)
-        torch.cuda.synchronize()
-        e1b = torch.cuda.Event(enable_timing=True)
-        e1b.record()
-        verify()
-        e2.record()
-        torch.cuda.synchronize()
-        cold_p.append(e0.elapsed_time(e1) * 1e-3)
-        cold_v.append(e1b.elapsed_time(e2) * 1e-3)
-    del flush
+    # The two kernels of the prefill call, each timed as its own call (same arguments).
+    us_intra = median_call_us(lambda: long("intra"), iters)
+    us_scan = median_call_us(lambda: long("scan"), iters)
+    log(f"split: intra {us_intra:.1f} us  scan {us_scan:.1f} us")
 
+    p_bytes, p_flops = long.alg()
     token_heads = T * H
-    prefill_bytes = token_heads * BYTES_PER_TOKEN_HEAD + N * H * STATE_BYTES   # + final states
-    intra_bytes = token_heads * (3 * 2 * D + 2)                                 # q, k, g, beta logit
-    scan_bytes = token_heads * (2 * D + 2 * D) + N * H * STATE_BYTES            # v, out, final states
+    intra_bytes = token_heads * (3 * 2 * D + 2)                      # q, k, g, beta logit
+    scan_bytes = token_heads * (2 * D + 2 * D) + N * H * STATE_BYTES  # v, out, final states
     verify_bytes = (B * Tv * H * BYTES_PER_TOKEN_HEAD + B * H * STATE_BYTES
                     + B * Tv * H * STATE_BYTES)
-    prefill_flops = token_heads * FLOPS_PER_TOKEN_HEAD
-    kernels = {
-        "kda_prefill_intra": (s_intra, roofline(intra_bytes, 0, s_intra)),
-        "kda_prefill_scan": (s_scan, roofline(scan_bytes, 0, s_scan)),
-        "kda_verify": (s_ver, roofline(verify_bytes, 0, s_ver)),
-    }
     workload = MAIN_WORKLOAD
-    for k, (_, rl_k) in kernels.items():
-        rl_k["traffic"] = stored_traffic(k, workload)
-    dom = max(kernels, key=lambda k: kernels[k][0])
-    rl = dict(kernels[dom][1])
-    rl["kernel"] = dom
-
-    log("measured ceilings (fill, copy, GEMM)")
-    ceil = measured_ceilings()
-    rl_p_hbm = roofline(prefill_bytes, 0, s_prefill)
-    rl_p_mfma = roofline(0, prefill_flops, s_prefill, bound="mfma")
-    vs_measured = {
-        "verify_vs_write_only": round(kernels["kda_verify"][1]["achieved"] / ceil["write_only_GBs"], 4),
-        "prefill_hbm_vs_copy": round(rl_p_hbm["achieved"] / ceil["copy_GBs"], 4),
-        "prefill_mfma_vs_gemm": round(rl_p_mfma["achieved"] / ceil["gemm_bf16_TFs"], 4),
+    by_kernel = {
+        "kda_prefill_intra": roofline(intra_bytes, 0, us_intra * 1e-6),
+        "kda_prefill_scan": roofline(scan_bytes, 0, us_scan * 1e-6),
+        "kda_verify": roofline(verify_bytes, 0, s_ver),
     }
+    for k, rl_k in by_kernel.items():
+        rl_k["traffic"] = stored_traffic(k, workload)
+    # The headline roofline is the prefill call's: its algorithmic bytes over the call's
+    # time (both kernels), with the calibrated traffic of both kernels per call.
+    rl = roofline(p_bytes, 0, s_prefill)
+    ti, ts_ = stored_traffic("kda_prefill_intra", workload), stored_traffic("kda_prefill_scan", workload)
+    rl["traffic"] = (ti + ts_) if ti is not None and ts_ is not None else None
+    rl["kernel"] = "kda_chunk_prefill (kda_prefill_intra + kda_prefill_scan)"
 
-    log("verify latency case (B = 1)")
-    lat_b1 = verify_latency_b1(args.steps)
+    configs = None
+    cold_verify = None
+    ceil = None
+    lat_b1 = None
+    if not args.no_extras:
+        flush = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+        log("protocol: medians of %d calls, warm and cold" % iters)
+        cold = lambda fn: {"write_flush": cold_call_us(fn, 10, flush, "write"),
+                           "read_flush": cold_call_us(fn, 10, flush, "read")}
+        configs = {}
+        us2 = median_call_us(long, iters)
+        configs["long_4x8192"] = config_line(W.LONG.name, us2, T, p_bytes, p_flops, cold(long),
+                                             {"intra_us": round(us_intra, 2),
+                                              "scan_us": round(us_scan, 2)})
+        us4 = median_call_us(verify, iters)
+        cold_verify = cold(verify)
+        configs["verify_64x8"] = config_line(vcase.name, us4, B * Tv, verify_bytes, 0, cold_verify)
+        long.free()
+        del vd, vout, inter
+        torch.cuda.empty_cache()
+        for key, case in (("varlen_8x2048", W.VARLEN), ("single_16384", W.SINGLE_LONG)):
+            log(f"protocol: {case.name}")
+            run = PrefillRun(case)
+            us = median_call_us(run, iters)
+            ui = median_call_us(lambda: run("intra"), iters)
+            uscan = median_call_us(lambda: run("scan"), iters)
+            b_, f_ = run.alg()
+            configs[key] = config_line(case.name, us, run.T, b_, f_, cold(run),
+                                       {"intra_us": round(ui, 2), "scan_us": round(uscan, 2)})
+            run.free()
+        del flush
+        torch.cuda.empty_cache()
+        log("verify latency case (B = 1)")
+        lat_b1 = verify_latency_b1(iters)
+        log("measured ceilings (fill, copy, GEMM)")
+        ceil = measured_ceilings()
 
     cpu = None
     if not args.no_cpu_baseline:
         log(f"oracle baseline on {args.cpu_tokens} tokens/sequence")
-        cpu = cpu_baseline(pcase, args.cpu_tokens)
+        cpu = cpu_baseline(W.LONG, args.cpu_tokens)
 
-    extras = None if args.no_extras else bench_next_rows(args.steps)
+    extras = None if args.no_extras else bench_next_rows(iters)
     if extras:
         log(f"commit {extras['commit']['us']} us  mixed step {extras['mixed_step']['us']} us")
 
@@ -713,27 +789,34 @@ def main():
         "prefill_tokens_per_s": round(value, 1),
         "verify_us_per_layer": round(s_ver * 1e6, 2),
         "verify_tokens_per_s": round(B * Tv / s_ver, 1),
-        "kernel_us": {"kda_prefill_intra": round(s_intra * 1e6, 2),
-                      "kda_prefill_scan": round(s_scan * 1e6, 2),
+        "timing": f"medians of per-call HIP events over the {args.steps} timed steps; "
+                  f"kernel split and configurations: medians of {iters} calls",
+        "kernel_us": {"kda_prefill_intra": round(us_intra, 2),
+                      "kda_prefill_scan": round(us_scan, 2),
                       "kda_verify": round(s_ver * 1e6, 2)},
-        "verify_latency_b1": lat_b1,
-        "cold_cache_us": {"prefill": round(float(np.median(cold_p)) * 1e6, 2),
-                          "verify": round(float(np.median(cold_v)) * 1e6, 2)},
         "roofline": rl,
-        "roofline_by_kernel": {k: v[1] for k, v in kernels.items()},
+        "roofline_by_kernel": by_kernel,
         "roofline_prefill_call": {
-            "hbm": rl_p_hbm,
-            "mfma": rl_p_mfma,
-            "roofline_frac": round(max(prefill_bytes / (HBM_PEAK_GBS * 1e9),
-                                       prefill_flops / (MFMA_BF16_PEAK_TFS * 1e12)) / s_prefill, 4),
+            "hbm": roofline(p_bytes, 0, s_prefill),
+            "mfma": roofline(0, p_flops, s_prefill, bound="mfma"),
+            "roofline_frac": round(max(p_bytes / (HBM_PEAK_GBS * 1e9),
+                                       p_flops / (MFMA_BF16_PEAK_TFS * 1e12)) / s_prefill, 4),
         },
+        "configs": configs,
+        "verify_latency_b1": lat_b1,
         "measured_ceilings": ceil,
-        "fraction_of_measured": vs_measured,
         "cpu_baseline": cpu,
         "next_rows": extras,
-        "context": {"flashkda_gb300_us_per_layer_8192x4": 146,
-                    "note": "the pages' number, other hardware; not a target"},
+        "context": {"flashkda_gb300_us_per_layer": {"2048x8": 49, "8192x4": 146, "16384x1": 787},
+                    "note": "the pages' numbers, other hardware; not targets"},
     }
+    if ceil:
+        res["fraction_of_measured"] = {
+            "verify_vs_write_only": round(by_kernel["kda_verify"]["achieved"] / ceil["write_only_GBs"], 4),
+            "prefill_hbm_vs_copy": round(rl["achieved"] / ceil["copy_GBs"], 4),
+            "prefill_mfma_vs_gemm": round(res["roofline_prefill_call"]["mfma"]["achieved"]
+                                          / ceil["gemm_bf16_TFs"], 4),
+        }
     print(json.dumps(res), flush=True)
 
 
