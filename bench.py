@@ -43,7 +43,7 @@ sys.path.insert(0, ROOT)
 from linear_attention_rule_amd import (causal_conv1d_prefill,  # noqa: E402
                                        causal_conv1d_update, chunk_prefill, commit_accepted,
                                        gated_rmsnorm, prefill_workspace_bytes,
-                                       recurrent_verify)
+                                       recurrent_verify, recurrent_verify_gated)
 from linear_attention_rule_amd import workloads as W  # noqa: E402
 
 METRIC = "KDA prefill µs/layer & tokens/s (8192x4, H=16, d=128); verify µs/layer"
@@ -426,6 +426,34 @@ def bench_next_rows(iters):
     commit_bytes = B * H * 2 * STATE_BYTES + 2 * B * 4
     del inter, pool
 
+    # Verify with the output-gate norm fused into its store, against verify then the
+    # standalone norm over its output, at the verify size and at batch 1.
+    gated = {}
+    for vc in (W.VERIFY, W.VERIFY_B1):
+        vd = to_dev(W.make_verify(vc))
+        Bv, Tg, Hv = vc.batch, vc.steps, vc.heads
+        nd = W.make_norm(W.NormCase("verify_gate", Bv * Tg, Hv, seed=4400))
+        gate, wgt = nd["gate"].cuda(), nd["weight"].cuda()
+        o_ = torch.empty((Bv * Tg, Hv, D), dtype=torch.bfloat16, device="cuda")
+        y_ = torch.empty_like(o_)
+        it_ = torch.empty((Bv, Tg, Hv, D, D), dtype=torch.float32, device="cuda")
+        r_ = torch.empty((Bv * Tg, Hv), dtype=torch.float32, device="cuda")
+        args_ = (vd["q"], vd["k"], vd["v"], vd["g"], vd["beta_logits"], vd["A_log"],
+                 vd["dt_bias"], vd["lower_bound"], vd["state_pool"], vd["state_idx"], Tg)
+
+        def fused():
+            recurrent_verify_gated(*args_, gate, wgt, nd["eps"], intermediate=it_, out=y_,
+                                   rstd=r_, scale=vd["scale"])
+
+        def separate():
+            recurrent_verify(*args_, intermediate=it_, out=o_, scale=vd["scale"])
+            gated_rmsnorm(o_, gate, wgt, nd["eps"], out=y_, rstd=r_)
+
+        gated[vc.name] = {"fused_us": round(median_call_us(fused, iters), 2),
+                          "verify_then_norm_us": round(median_call_us(separate, iters), 2)}
+        del vd, o_, y_, it_, r_
+    torch.cuda.empty_cache()
+
     m = W.make_mixed(W.MIXED)
     pre, spec = to_dev(m["prefill"]), to_dev(m["spec"])
     Tp, Hm = pre["q"].shape[0], pre["q"].shape[1]
@@ -501,6 +529,7 @@ def bench_next_rows(iters):
                         "roofline": rl_convu, "algorithmic_bytes": convu_bytes},
         "gated_rmsnorm": {"workload": W.NORM.name, "us": round(t_norm * 1e6, 2),
                           "roofline": rl_norm, "algorithmic_bytes": norm_bytes},
+        "verify_gated_norm": gated,
         "mixed_step": {"workload": W.MIXED.name, "us": round(t_mixed * 1e6, 2),
                        "tokens_per_s": round(tokens / t_mixed, 1),
                        "roofline": roofline(mixed_bytes, 0, t_mixed),

@@ -213,6 +213,36 @@ kda_status kda_recurrent_verify(const void* q, const void* k, const void* v, con
                                 const int32_t* state_idx, float* intermediate_state, void* out,
                                 const kda_verify_desc* desc, void* stream);
 
+/* The output-gate sigmoid RMSNorm applied to each output row before it is stored
+ * (SGLang PR #42489 "Improve GLM-5.3-Flash DFlash decoding on B300": the sigmoid
+ * RMSNorm of the attention output, tuned with the recurrence).  For output row r and
+ * head h, with o the fp32 output of the recurrence (scale included):
+ *     rstd = 1 / sqrt(mean(o^2) + eps),   y = o * rstd * weight * sigmoid(gate[r, h])
+ * and y, rounded to bf16, is what lands in out.  Rows are the output rows (the token
+ * index, or out_token_index[token] when the descriptor scatters). */
+typedef struct kda_output_norm {
+  const void* gate;            /* bf16 [out rows, H, 128], token-strided, 16-byte aligned */
+  int64_t gate_token_stride;   /* elements, 0 = H*128; a multiple of 8 */
+  const float* weight;         /* fp32 [128], shared by the heads, 16-byte aligned */
+  float eps;                   /* finite, >= 0 */
+  float* rstd;                 /* fp32 [out rows, H], or NULL (not written) */
+} kda_output_norm;
+
+/*
+ * kda_recurrent_verify with the output-gate sigmoid RMSNorm fused into its output
+ * store (one launch: the normalised rows never pass through memory unnormalised).
+ * Arguments and checks are those of kda_recurrent_verify plus `norm` (not NULL); gate,
+ * weight and rstd must not overlap out or the state buffers.  Padding rows store
+ * y = 0 and rstd = 1/sqrt(eps).
+ */
+kda_status kda_recurrent_verify_gated(const void* q, const void* k, const void* v, const void* g,
+                                      const void* beta_logits, const float* A_log,
+                                      const float* dt_bias, float lower_bound,
+                                      const float* state_pool, const int32_t* state_idx,
+                                      float* intermediate_state, void* out,
+                                      const kda_output_norm* norm, const kda_verify_desc* desc,
+                                      void* stream);
+
 /*
  * Commit after verify: the num_accepted_tokens rollback of vLLM PR #55737
  * ("...code steps too" commit message: spec-decode tokens keep the recurrent

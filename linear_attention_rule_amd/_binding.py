@@ -48,6 +48,11 @@ class VerifyDesc(ctypes.Structure):
                 ("out_token_index", ctypes.c_void_p), ("out_rows", ctypes.c_int64)]
 
 
+class OutputNorm(ctypes.Structure):
+    _fields_ = [("gate", ctypes.c_void_p), ("gate_token_stride", ctypes.c_int64),
+                ("weight", ctypes.c_void_p), ("eps", ctypes.c_float), ("rstd", ctypes.c_void_p)]
+
+
 class CommitDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("num_steps", ctypes.c_int32),
                 ("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
@@ -107,6 +112,10 @@ def load_library(path: str | None = None):
     lib.kda_recurrent_verify.restype = ctypes.c_int
     lib.kda_recurrent_verify.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp,
                                          ctypes.POINTER(VerifyDesc), vp]
+    lib.kda_recurrent_verify_gated.restype = ctypes.c_int
+    lib.kda_recurrent_verify_gated.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp,
+                                               ctypes.POINTER(OutputNorm),
+                                               ctypes.POINTER(VerifyDesc), vp]
     lib.kda_commit_accepted.restype = ctypes.c_int
     lib.kda_commit_accepted.argtypes = [vp, vp, vp, vp, ctypes.POINTER(CommitDesc), vp]
     lib.kda_causal_conv1d_prefill.restype = ctypes.c_int
@@ -350,6 +359,63 @@ def recurrent_verify(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, state
                                   ctypes.byref(desc), _stream_handle(dev))
     _check(st)
     return out, intermediate
+
+
+def recurrent_verify_gated(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, state_pool,
+                           state_idx, num_steps, out_gate, norm_weight, norm_eps, *,
+                           intermediate=None, out=None, rstd=None, want_rstd=True, scale=None,
+                           out_token_index=None):
+    """Fused multi-step verify with the output-gate sigmoid RMSNorm applied to each output
+    row before it is stored (kda_recurrent_verify_gated).  Returns (y [B*T or rows, H, 128]
+    bf16, intermediate, rstd [rows, H] f32 or None).
+
+    out_gate: bf16 [rows, H, 128] (token stride free, heads dense), one row per output row
+    (rows = B*T, or out.shape[0] with out_token_index); norm_weight: f32 [128].
+    """
+    lib = load_library()
+    BT, H = int(q.shape[0]), int(q.shape[1])
+    T = int(num_steps)
+    if T < 1 or BT % T:
+        raise ValueError("token count must be a multiple of num_steps")
+    B = BT // T
+    qs = _token_tensor("q", q, H, HEAD_DIM)
+    ks = _token_tensor("k", k, H, HEAD_DIM)
+    vs = _token_tensor("v", v, H, HEAD_DIM)
+    gs = _token_tensor("g", g, H, HEAD_DIM)
+    bs = _token_tensor("beta_logits", beta_logits, H, None)
+    _f32("A_log", A_log, (H,))
+    _f32("dt_bias", dt_bias, (H, HEAD_DIM))
+    slots = int(state_pool.shape[0])
+    _f32("state_pool", state_pool, (slots, H, HEAD_DIM, HEAD_DIM))
+    _i32("state_idx", state_idx, B)
+    _f32("norm_weight", norm_weight, (HEAD_DIM,))
+    dev = q.device
+    if out is None:
+        if out_token_index is not None:
+            raise ValueError("out_token_index needs the destination buffer `out`")
+        out = torch.empty((BT, H, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+    os_, out_rows, oidx = _out_index(out, out_token_index, BT, H)
+    rows = int(out.shape[0])
+    ogs = _token_tensor("out_gate", out_gate, H, HEAD_DIM)
+    if out_gate.shape[0] != rows:
+        raise ValueError(f"out_gate must have {rows} rows (one per output row)")
+    if intermediate is None:
+        intermediate = torch.empty((B, T, H, HEAD_DIM, HEAD_DIM), dtype=torch.float32, device=dev)
+    _f32("intermediate", intermediate, (B, T, H, HEAD_DIM, HEAD_DIM))
+    if rstd is None and want_rstd:
+        rstd = torch.empty((rows, H), dtype=torch.float32, device=dev)
+    if rstd is not None:
+        _f32("rstd", rstd, (rows, H))
+    norm = OutputNorm(_ptr(out_gate), ogs, _ptr(norm_weight), float(norm_eps), _ptr(rstd))
+    desc = VerifyDesc(B, T, H, HEAD_DIM, float(scale) if scale else 0.0, slots,
+                      qs, ks, vs, gs, bs, os_, oidx, out_rows)
+    st = lib.kda_recurrent_verify_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta_logits),
+                                        _ptr(A_log), _ptr(dt_bias), float(lower_bound),
+                                        _ptr(state_pool), _ptr(state_idx), _ptr(intermediate),
+                                        _ptr(out), ctypes.byref(norm), ctypes.byref(desc),
+                                        _stream_handle(dev))
+    _check(st)
+    return out, intermediate, rstd
 
 
 def commit_accepted(intermediate, state_idx, num_accepted, state_pool):

@@ -303,11 +303,15 @@ kda_status kda_chunk_prefill_noalloc(const void* q, const void* k, const void* v
                         stream, kda::PHASE_INTRA | kda::PHASE_SCAN, /*use_scratch=*/true);
 }
 
-kda_status kda_recurrent_verify(const void* q, const void* k, const void* v, const void* g,
-                                const void* beta_logits, const float* A_log, const float* dt_bias,
-                                float lower_bound, const float* state_pool,
-                                const int32_t* state_idx, float* intermediate_state, void* out,
-                                const kda_verify_desc* desc, void* stream) {
+}  // extern "C"
+
+namespace {
+
+kda_status verify_impl(const void* q, const void* k, const void* v, const void* g,
+                       const void* beta_logits, const float* A_log, const float* dt_bias,
+                       float lower_bound, const float* state_pool, const int32_t* state_idx,
+                       float* intermediate_state, void* out, const kda_output_norm* norm,
+                       const kda_verify_desc* desc, void* stream) {
   if (!desc) return fail(KDA_ERR_INVALID_ARGUMENT, "desc is NULL");
   const int B = desc->batch, T = desc->num_steps, H = desc->num_heads;
   if (desc->head_dim != KDA_HEAD_DIM)
@@ -365,6 +369,30 @@ kda_status kda_recurrent_verify(const void* q, const void* k, const void* v, con
       return fail(KDA_ERR_INVALID_ARGUMENT, "intermediate_state overlaps an input");
   if (overlaps(s_int, span_of(beta_logits, BT, bs, H, 2)))
     return fail(KDA_ERR_INVALID_ARGUMENT, "intermediate_state overlaps beta_logits");
+  int64_t ngs = 0;
+  if (norm) {
+    // The fused output norm reads the gate rows of the output rows and writes rstd rows.
+    if (!norm->gate || !norm->weight)
+      return fail(KDA_ERR_INVALID_ARGUMENT, "norm gate / weight is NULL");
+    if (!std::isfinite(norm->eps) || norm->eps < 0.f)
+      return fail(KDA_ERR_INVALID_ARGUMENT, "norm eps must be finite and >= 0");
+    if (kda_status st = check_stride("norm gate", norm->gate_token_stride, HD, HD, &ngs)) return st;
+    if (!aligned16(norm->gate) || !aligned16(norm->weight) || (ngs & 7))
+      return fail(KDA_ERR_INVALID_ARGUMENT,
+                  "norm gate / weight must be 16-byte aligned, gate stride a multiple of 8");
+    if (norm->rstd && (reinterpret_cast<uintptr_t>(norm->rstd) & 3u))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "rstd must be 4-byte aligned");
+    const Span s_gate = span_of(norm->gate, orows, ngs, HD, 2);
+    if (overlaps(so, s_gate)) return fail(KDA_ERR_INVALID_ARGUMENT, "out overlaps the norm gate");
+    if (overlaps(s_int, s_gate))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "intermediate_state overlaps the norm gate");
+    if (norm->rstd) {
+      const Span s_r = span_of(norm->rstd, orows * H, 1, 1, 4);
+      if (overlaps(s_r, so) || overlaps(s_r, s_gate) || overlaps(s_r, s_int) ||
+          overlaps(s_r, s_pool))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "rstd overlaps out, the gate or a state buffer");
+    }
+  }
 
   kda::VerifyParams p{};
   p.q = static_cast<const uint16_t*>(q);
@@ -387,9 +415,41 @@ kda_status kda_recurrent_verify(const void* q, const void* k, const void* v, con
   p.H = H;
   p.slots = desc->num_slots;
   p.q_st = qs; p.k_st = ks; p.v_st = vs; p.g_st = gs; p.b_st = bs; p.o_st = os;
+  if (norm) {
+    p.out_gate = static_cast<const uint16_t*>(norm->gate);
+    p.norm_w = norm->weight;
+    p.rstd = norm->rstd;
+    p.norm_eps = norm->eps;
+    p.og_st = ngs;
+  }
   const hipError_t e = kda::launch_verify(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "verify launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_recurrent_verify(const void* q, const void* k, const void* v, const void* g,
+                                const void* beta_logits, const float* A_log, const float* dt_bias,
+                                float lower_bound, const float* state_pool,
+                                const int32_t* state_idx, float* intermediate_state, void* out,
+                                const kda_verify_desc* desc, void* stream) {
+  return verify_impl(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, state_pool, state_idx,
+                     intermediate_state, out, nullptr, desc, stream);
+}
+
+kda_status kda_recurrent_verify_gated(const void* q, const void* k, const void* v, const void* g,
+                                      const void* beta_logits, const float* A_log,
+                                      const float* dt_bias, float lower_bound,
+                                      const float* state_pool, const int32_t* state_idx,
+                                      float* intermediate_state, void* out,
+                                      const kda_output_norm* norm, const kda_verify_desc* desc,
+                                      void* stream) {
+  if (!norm) return fail(KDA_ERR_INVALID_ARGUMENT, "norm is NULL");
+  return verify_impl(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, state_pool, state_idx,
+                     intermediate_state, out, norm, desc, stream);
 }
 
 }  // extern "C"

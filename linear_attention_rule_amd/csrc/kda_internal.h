@@ -92,6 +92,13 @@ struct VerifyParams {
   float scale;
   int B, T, H, slots;
   int64_t q_st, k_st, v_st, g_st, b_st, o_st;
+  // Output-gate sigmoid RMSNorm fused into the output store (null gate: plain output).
+  // gate and rstd rows are the output rows the tokens' outputs go to.
+  const uint16_t* out_gate;
+  const float* norm_w;
+  float* rstd;
+  float norm_eps;
+  int64_t og_st;
 };
 
 struct NormParams {

@@ -28,13 +28,20 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-template <int BV>
+// NORM: the output-gate sigmoid RMSNorm of each output row is applied before the store
+// (SGLang PR #42489, "Modifications": the sigmoid RMSNorm tuned together with the
+// recurrence).  It needs whole rows, so it runs with 128-column tiles only: each step
+// leaves its fp32 output row in LDS (in the step's dead decay-table row), and after the
+// last step groups of 32 threads normalise the rows and store y = o * rstd * weight *
+// sigmoid(gate), with the gate rows staged in the prologue.
+template <int BV, bool NORM>
 __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p) {
   constexpr int NCG = BV / 4;      // column groups (float4) per state row
   constexpr int NRG = 256 / NCG;   // row groups
   constexpr int R = D / NRG;       // rows per thread
   constexpr int NVT = D / BV;      // value tiles per head
   static_assert(R >= 1 && D % NRG == 0, "bad tile");
+  static_assert(!NORM || BV == D, "the fused norm needs whole rows");
 
   extern __shared__ float smem[];
   const int T = p.T;
@@ -46,6 +53,9 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p) {
   float* s_kq = s_beta + T;           // [T]
   float* s_part = s_kq + T;           // [2 parity][4 waves][2 (r, y)][BV]
   int* s_orow = reinterpret_cast<int*>(s_part + 2 * 4 * 2 * BV);   // [T] output rows
+  // NORM: the raw bf16 output-gate rows [T][128], 16-byte aligned after s_orow
+  uint16_t* s_gate = reinterpret_cast<uint16_t*>(
+      reinterpret_cast<uintptr_t>(s_orow + T + 3) & ~static_cast<uintptr_t>(15));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -59,12 +69,16 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p) {
 
   const int slot = p.idx[b];
   if (slot < 0 || slot >= p.slots) {
-    // Padding row: zero outputs, no state rows written.
+    // Padding row: zero outputs (normalised or not), no state rows written; the norm's
+    // rstd of a zero row is 1/sqrt(eps).
     for (int e = tid; e < T * BV; e += 256) {
       const int t = e / BV, c = e % BV;
       int64_t orow = static_cast<int64_t>(b) * T + t;
       if (p.out_idx) orow = p.out_idx[orow];
-      if (orow >= 0 && orow < p.out_rows) p.out[orow * p.o_st + h * D + v0 + c] = 0;
+      if (orow >= 0 && orow < p.out_rows) {
+        p.out[orow * p.o_st + h * D + v0 + c] = 0;
+        if (NORM && c == 0 && p.rstd) p.rstd[orow * p.H + h] = __builtin_amdgcn_rsqf(p.norm_eps);
+      }
     }
     return;
   }
@@ -99,6 +113,15 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p) {
     if (lane == 0) {
       s_beta[t] = sigmoid_f32(bf16_to_f32(p.beta[tok * p.b_st + h]));
       s_kq[t] = sqk * rq * rk;
+    }
+    if (NORM) {
+      // the output gate of this token's output row (rows outside the output are never
+      // stored; their gate is not read)
+      const int64_t orow = p.out_idx ? static_cast<int64_t>(p.out_idx[tok]) : tok;
+      uint32_t gw2 = 0;
+      if (orow >= 0 && orow < p.out_rows)
+        gw2 = *reinterpret_cast<const uint32_t*>(p.out_gate + orow * p.og_st + h * D + 2 * lane);
+      *reinterpret_cast<uint32_t*>(s_gate + t * D + 2 * lane) = gw2;
     }
   }
 
@@ -174,35 +197,72 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p) {
     }
     if (rg == 0) {
       const float s = p.scale;
-      const uint32_t w0 = pack_bf16x2(s * (yy.x + kq * u.x), s * (yy.y + kq * u.y));
-      const uint32_t w1 = pack_bf16x2(s * (yy.z + kq * u.z), s * (yy.w + kq * u.w));
+      const float4 o = make_float4(s * (yy.x + kq * u.x), s * (yy.y + kq * u.y),
+                                   s * (yy.z + kq * u.z), s * (yy.w + kq * u.w));
+      if (NORM) {
+        // Row t of the decay table is dead once this step's barrier has passed (every
+        // thread read its entries before it): the fp32 output row waits there for the norm.
+        *reinterpret_cast<float4*>(s_alpha + t * D + 4 * cl) = o;
+      } else {
+        const int64_t orow = s_orow[t];
+        if (orow >= 0 && orow < p.out_rows)
+          *reinterpret_cast<uint2*>(p.out + orow * p.o_st + h * D + v0 + 4 * cl) =
+              make_uint2(pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w));
+      }
+    }
+  }
+  if (NORM) {
+    // The norm of every output row after the last step, off the steps' critical path:
+    // groups of 32 threads take one row each (4 channels per thread), reduce its squares
+    // across the group and store y = o * rstd * weight * sigmoid(gate).
+    __syncthreads();
+    const int grp = tid >> 5, c4 = 4 * (tid & 31);
+    const float4 w4 = *reinterpret_cast<const float4*>(p.norm_w + c4);
+    for (int t = grp; t < T; t += 8) {
+      const float4 o = *reinterpret_cast<const float4*>(s_alpha + t * D + c4);
+      float ss = o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) ss += __shfl_xor(ss, off);
+      const float rs = __builtin_amdgcn_rsqf(ss * (1.0f / D) + p.norm_eps);
+      const uint2 gr = *reinterpret_cast<const uint2*>(s_gate + t * D + c4);
+      const float y0 = o.x * rs * w4.x * sigmoid_f32(bf16lo_to_f32(gr.x));
+      const float y1 = o.y * rs * w4.y * sigmoid_f32(bf16hi_to_f32(gr.x));
+      const float y2 = o.z * rs * w4.z * sigmoid_f32(bf16lo_to_f32(gr.y));
+      const float y3 = o.w * rs * w4.w * sigmoid_f32(bf16hi_to_f32(gr.y));
       const int64_t orow = s_orow[t];
-      if (orow >= 0 && orow < p.out_rows)
-        *reinterpret_cast<uint2*>(p.out + orow * p.o_st + h * D + v0 + 4 * cl) =
-            make_uint2(w0, w1);
+      if (orow >= 0 && orow < p.out_rows) {
+        *reinterpret_cast<uint2*>(p.out + orow * p.o_st + h * D + c4) =
+            make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
+        if ((tid & 31) == 0 && p.rstd) p.rstd[orow * p.H + h] = rs;
+      }
     }
   }
 }
 
-template <int BV>
+template <int BV, bool NORM>
 size_t verify_lds_bytes(int T) {
-  return sizeof(float) * (static_cast<size_t>(T) * (3 * D + BV) + 3 * T + 2 * 4 * 2 * BV);
+  const size_t base = sizeof(float) * (static_cast<size_t>(T) * (3 * D + BV) + 3 * T + 2 * 4 * 2 * BV);
+  // NORM: the gate rows as bf16 after 16-byte alignment (fits 160 KiB at 64 steps)
+  return NORM ? ((base + 15) & ~size_t{15}) + static_cast<size_t>(T) * D * 2 : base;
 }
+static_assert(sizeof(float) * (64 * (3 * D + D) + 3 * 64 + 2 * 4 * 2 * D) + 16 + 64 * D * 2 <=
+                  160 * 1024,
+              "the fused-norm verify's LDS at the largest step count exceeds 160 KiB");
 
-template <int BV>
+template <int BV, bool NORM>
 hipError_t launch_verify_bv(const VerifyParams& p, hipStream_t s) {
-  const size_t lds = verify_lds_bytes<BV>(p.T);
+  const size_t lds = verify_lds_bytes<BV, NORM>(p.T);
   // The LDS limit for the largest step count is set once per device, not per call
   // (verify at batch 1 is latency-bound).
   static PerDeviceOnce attr_once;
   hipError_t e = attr_once.run([](int, int*) {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(&verify_kernel<BV>),
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(&verify_kernel<BV, NORM>),
                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                               static_cast<int>(verify_lds_bytes<BV>(KDA_MAX_STEPS_INTERNAL)));
+                               static_cast<int>(verify_lds_bytes<BV, NORM>(KDA_MAX_STEPS_INTERNAL)));
   });
   if (e != hipSuccess) return e;
   const dim3 grid(static_cast<unsigned>(p.B) * p.H * (D / BV));
-  hipLaunchKernelGGL(verify_kernel<BV>, grid, dim3(256), lds, s, p);
+  hipLaunchKernelGGL((verify_kernel<BV, NORM>), grid, dim3(256), lds, s, p);
   return hipGetLastError();
 }
 
@@ -210,10 +270,12 @@ hipError_t launch_verify_bv(const VerifyParams& p, hipStream_t s) {
 
 hipError_t launch_verify(const VerifyParams& p, hipStream_t s) {
   if (p.B == 0) return hipSuccess;
+  // The fused output norm needs whole 128-column rows in one workgroup.
+  if (p.out_gate) return launch_verify_bv<128, true>(p, s);
   // Enough workgroups to cover the 256 compute units: split each head's value
   // columns four ways when there are few (row, head) pairs.
-  if (static_cast<int64_t>(p.B) * p.H >= 256) return launch_verify_bv<128>(p, s);
-  return launch_verify_bv<32>(p, s);
+  if (static_cast<int64_t>(p.B) * p.H >= 256) return launch_verify_bv<128, false>(p, s);
+  return launch_verify_bv<32, false>(p, s);
 }
 
 }  // namespace kda
