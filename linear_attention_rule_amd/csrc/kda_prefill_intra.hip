@@ -26,9 +26,10 @@
 //   are formed per 16-token row block m with the block's start as reference:
 //   left factor 2^(b_t - base_m) <= 1 and right factor 2^(base_m - b_i), which
 //   is <= 1 off the diagonal and <= 2^(16*5*log2 e) < 2^116 on it -- inside the
-//   bf16/fp32 exponent range for lower_bound >= -5.  G uses bf16 operands; P
-//   uses a three-product bf16 split (hi*hi + hi*lo + lo*hi), since its rounding
-//   reaches the output directly.
+//   bf16/fp32 exponent range for lower_bound >= -5.  Off the diagonal both factors
+//   are <= 1, so G and P take one fp16 product each (11-bit mantissa); on the
+//   diagonal G uses bf16 operands and P a three-product bf16 split (hi*hi + hi*lo
+//   + lo*hi), since its rounding reaches the output directly.
 #include "kda_prefill_common.h"
 
 namespace kda {
@@ -95,7 +96,9 @@ struct IntraSmem {
   float AT[64 * ATS];          // A = diag(beta) strict(G), inverted in place into T
   float P[64 * ATS];           // scale * tril(P)
   union {
-    float R0[3 * 4 * 64 * 8];  // right factors of row blocks 0..2 (fp32), by (block, s, lane, e)
+    // fp16 right factors of row blocks w = 0..2 re-referenced to each later row block m
+    // (both factors of an off-diagonal block are <= 1), by (pair(m, w), k-step s, lane)
+    half8 R16[6][4][64];
     struct {
       _Float16 KCt[128 * KCS]; // K_C transposed [channel][token]
       float tmp[3][256];       // 16x16 partial products of the block inverse
@@ -256,6 +259,7 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
 
   // ---- operands.  b = la (in-block cumulative), Lf = 2^b <= 1, Rf = 2^-b >= 1.
   bf16x8 KL[4], QLh[4], QLl[4], Rh[4], Rl[4];
+  half8 KL16[4], QL16[4];   // the left factors in fp16, for the off-diagonal blocks
   _Float16 kch[32];
   {
     const float rqs = rq * p.scale;
@@ -290,7 +294,7 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
         kch[i] = static_cast<_Float16>(kcv[i] * kr);
         klv[e] = kl;
         qlv[e] = ql;
-        kv[i] = kr;  // the fp32 right factor, kept for publication
+        kv[i] = kr;  // the fp32 right factor (the diagonal split and the off-diagonal fp16)
       }
       u32x4 klp, qhp, qlp, rhp, rlp;
 #pragma unroll
@@ -305,6 +309,26 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
         rlp[j] = lo;
       }
       KL[s] = as_bf16x8(klp);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        KL16[s][e] = static_cast<_Float16>(klv[e]);
+        QL16[s][e] = static_cast<_Float16>(qlv[e]);
+      }
+      // Off-diagonal right factors, made here by the wave that owns the column block: for
+      // each later row block m, k^ 2^(base_w - b_i) * 2^(base_m - base_w) = k^ 2^(base_m - b_i)
+      // <= 1, rounded to fp16 (its 11-bit mantissa beats bf16; the range is fine).  Wave w
+      // makes 3 - w of them and consumes w, so the waves share the off-diagonal work evenly.
+      for (int mm = w + 1; mm < 4; ++mm) {
+        const float* dsc = sm.Dsc[pair_idx(mm, w)];
+        const float4 d0 = *reinterpret_cast<const float4*>(dsc + kperm(s, g, 0));
+        const float4 d1 = *reinterpret_cast<const float4*>(dsc + kperm(s, g, 4));
+        const float* r = kv + 8 * s;
+        const half8 hr = {static_cast<_Float16>(r[0] * d0.x), static_cast<_Float16>(r[1] * d0.y),
+                          static_cast<_Float16>(r[2] * d0.z), static_cast<_Float16>(r[3] * d0.w),
+                          static_cast<_Float16>(r[4] * d1.x), static_cast<_Float16>(r[5] * d1.y),
+                          static_cast<_Float16>(r[6] * d1.z), static_cast<_Float16>(r[7] * d1.w)};
+        sm.u.R16[pair_idx(mm, w)][s][lane] = hr;
+      }
       QLh[s] = as_bf16x8(qhp);
       QLl[s] = as_bf16x8(qlp);
       Rh[s] = as_bf16x8(rhp);
@@ -313,62 +337,30 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
       rec_store(rec + (FR_QG + 4 * w + s) * 1024 + lane * 16, qg);
     }
   }
-  if (w < 3) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      float* dst = sm.u.R0 + ((w * 4 + s) * 64 + lane) * 8;
-      *reinterpret_cast<float4*>(dst) = make_float4(kv[8 * s], kv[8 * s + 1], kv[8 * s + 2], kv[8 * s + 3]);
-      *reinterpret_cast<float4*>(dst + 4) =
-          make_float4(kv[8 * s + 4], kv[8 * s + 5], kv[8 * s + 6], kv[8 * s + 7]);
-    }
-  }
   lds_barrier();
 
-  // ---- a2: G and P for row block w, column blocks 0..w (MFMA).
+  // ---- a2: G and P for row block w, column blocks 0..w (MFMA).  Off the diagonal one
+  // fp16 product each (factors <= 1); on it bf16 (the right factor reaches 2^115): G one
+  // product, P the three-product split.
   for (int wb = 0; wb <= w; ++wb) {
     f32x4 accG = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
-    bf16x8 bh[4], bl[4];
     if (wb == w) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        bh[s] = Rh[s];
-        bl[s] = Rl[s];
+        accG = mfma_bf16(KL[s], Rh[s], accG);
+        accP = mfma_bf16(QLh[s], Rh[s], accP);
+        accP = mfma_bf16(QLh[s], Rl[s], accP);
+        accP = mfma_bf16(QLl[s], Rh[s], accP);
       }
     } else {
-      // All of this block's LDS reads first (16-byte vectors), then the splits.
-      float4 sv[4][2], dv[4][2];
-      const float* dsc = sm.Dsc[pair_idx(w, wb)];
+      half8 rf[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) rf[s] = sm.u.R16[pair_idx(w, wb)][s][lane];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const float* src = sm.u.R0 + ((wb * 4 + s) * 64 + lane) * 8;
-        sv[s][0] = *reinterpret_cast<const float4*>(src);
-        sv[s][1] = *reinterpret_cast<const float4*>(src + 4);
-        dv[s][0] = *reinterpret_cast<const float4*>(dsc + kperm(s, g, 0));
-        dv[s][1] = *reinterpret_cast<const float4*>(dsc + kperm(s, g, 4));
+        accG = mfma_f16(KL16[s], rf[s], accG);
+        accP = mfma_f16(QL16[s], rf[s], accP);
       }
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        u32x4 hp, lp;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          uint32_t hi, lo;
-          split_bf16x2(sv[s][q].x * dv[s][q].x, sv[s][q].y * dv[s][q].y, hi, lo);
-          hp[2 * q] = hi;
-          lp[2 * q] = lo;
-          split_bf16x2(sv[s][q].z * dv[s][q].z, sv[s][q].w * dv[s][q].w, hi, lo);
-          hp[2 * q + 1] = hi;
-          lp[2 * q + 1] = lo;
-        }
-        bh[s] = as_bf16x8(hp);
-        bl[s] = as_bf16x8(lp);
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      accG = mfma_bf16(KL[s], bh[s], accG);
-      accP = mfma_bf16(QLh[s], bh[s], accP);
-      accP = mfma_bf16(QLh[s], bl[s], accP);
-      accP = mfma_bf16(QLl[s], bh[s], accP);
     }
     // lane (n, g) holds rows t = 16w + 4g + r, column i = 16wb + n
     const int i = 16 * wb + m;
@@ -394,7 +386,7 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
       sm.P[tr * ATS + i] = 0.f;
     }
   }
-  lds_barrier();   // R0 is dead from here on; the union's late view may be written
+  lds_barrier();   // R16 is dead from here on; the union's late view may be written
 
   // K_C transposed into LDS ([channel][token]) for the K_C^T fragments.
 #pragma unroll

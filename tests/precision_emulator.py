@@ -5,14 +5,18 @@ operands rounded to 16-bit formats.  This module replays that chunked form in
 float64 with exactly those rounding points, so the error each format choice costs
 can be measured against the fp64 token-loop oracle without a GPU:
 
-* G (k.k Gram, feeds the UT transform): bf16 operands, one product;
-* P (q.k Gram, feeds the output directly): bf16 hi/lo split, three products;
+* G (k.k Gram, feeds the UT transform): bf16 operands, one product, on the diagonal
+  16-token blocks; fp16 operands off them (both factors <= 1 there);
+* P (q.k Gram, feeds the output directly): bf16 hi/lo split, three products, on the
+  diagonal blocks; one fp16 product off them;
 * T = (I + diag(beta) strict(G))^-1 and everything on the fp32 VALU: kept in float64;
 * the scan operands -K_Gamma, T diag(beta), scale Q_Gamma, scale tril(P), K_C^T and
   the per-chunk S, X = V - K_Gamma S, U = T'X: fp16, with fp32 accumulation;
 * the output: bf16 round-to-nearest-even.
 
-Variants swap one choice (plain bf16 P; bf16 scan operands) to show what it costs.
+Variants swap one choice to show what it costs: "bf16_offdiag" (the off-diagonal blocks
+in bf16 like the diagonal ones), "plain_bf16_P" (no split anywhere), "bf16_scan" (bf16 scan
+operands).
 The chunked form itself is derived from the recurrence in tests/chunkform_fp64.py's
 terms; the 16-token row blocks with block-start references are how the GPU keeps
 every exponential inside the bf16/fp16 exponent range.  Nothing here is shared with
@@ -87,6 +91,12 @@ def _chunk_record(qn, kn, la2, beta, scale, variant):
         for w in range(m + 1):
             ic = slice(w * BLOCK, min(L, (w + 1) * BLOCK))
             right = kr[ic] * 2.0 ** (base[m] - base[w])       # re-referenced to block m
+            if variant in ("gpu", "bf16_scan") and w < m:
+                # both factors <= 1 off the diagonal: one fp16 product each for G and P
+                Rf16 = f16(right)
+                G[tr, ic] = f16(kl[tr]) @ Rf16.T
+                P[tr, ic] = f16(ql[tr]) @ Rf16.T
+                continue
             Rh, Rl = _split_bf16(right)
             G[tr, ic] = KL[tr] @ Rh.T
             if variant == "plain_bf16_P":
@@ -116,7 +126,7 @@ def emulate_prefill(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, cu_seq
     Arrays as in the oracle (float64 values of the bf16 inputs): q, k, g [T, H, 128];
     v [T, H, 128]; beta_logits [T, H]; A_log [H]; dt_bias [H, 128]; cu_seqlens [N+1];
     initial_state [N, H, 128, 128] or None.  variant: "gpu" (the formats the kernels
-    use), "plain_bf16_P" or "bf16_scan".
+    use), "bf16_offdiag", "plain_bf16_P" or "bf16_scan".
     Returns (out [T, H, 128] bf16-rounded, final [N, H, 128, 128], stats) where stats
     holds the largest |value| entering each fp16 operand: "S", "X", "U".
     """

@@ -50,6 +50,23 @@ def test_kernel_formats_meet_the_bar(lens, H, init):
     assert r <= 0.5 * TOL.STATE_TOL
 
 
+def test_fp16_off_diagonal_blocks_cost_nothing():
+    # off the diagonal both Gram factors are <= 1: fp16 (one product) is as good as bf16
+    for lb in (-5.0, 0.0):
+        d = W.make_prefill(W.PrefillCase("offdiag", [1024], 2, seed=7124, lower_bound=lb))
+        f = W.to_f64
+        args = (f(d["q"]), f(d["k"]), f(d["v"]), f(d["g"]), f(d["beta_logits"]), f(d["A_log"]),
+                f(d["dt_bias"]), d["lower_bound"], d["cu_seqlens"].numpy())
+        o_ref, f_ref = O.chunk_prefill(*args, None, scale=d["scale"])
+        res = {}
+        for var in ("gpu", "bf16_offdiag"):
+            o, fin, _ = E.emulate_prefill(*args, None, scale=d["scale"], variant=var)
+            res[var] = (TOL.output_errors(o, o_ref)["excess_over_rms"], TOL.state_rel_l2(fin, f_ref))
+        print(lb, res)
+        assert res["gpu"][0] <= 1.05 * res["bf16_offdiag"][0]
+        assert res["gpu"][1] <= 1.05 * res["bf16_offdiag"][1]
+
+
 def test_plain_bf16_P_fails_the_output_bar():
     e, r, _, _ = _errors([2048], 2, "per_seq", 9048, "plain_bf16_P")
     e_ok, _, _, _ = _errors([2048], 2, "per_seq", 9048, "gpu")
