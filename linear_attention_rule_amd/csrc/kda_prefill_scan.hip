@@ -681,52 +681,74 @@ void prefill_scan_kernel(PrefillParams p) {
 }
 
 // Segment start states: S_in(1) comes from segment 0; then, for each middle segment s in
-// order, S_in(s+1) = M_s S_in(s) + B_s in fp32.  One workgroup of 1024 threads per
-// (sequence, head, 32-column slice); thread t computes row t/8 and columns 4(t%8) .. +3 of
-// the slice, reading its row of M_s from global memory (L2: the four slices of a pair
-// share it) and the slice of S_in(s) from LDS.  The few workgroups leave most CUs idle,
-// so 16 waves each hide the load latency (1 x 16384 x 16 heads: 26 -> 15 us against 256
-// threads with 4 rows each).
+// order, S_in(s+1) = M_s S_in(s) + B_s, as fp32 MFMA products (v_mfma_f32_16x16x4_f32:
+// fp32 operands, fp32 accumulation).  One workgroup of 16 waves per (sequence, head,
+// 32-column slice); wave w computes the 16x16 output tile (rows 16(w/2).., columns
+// 16(w%2).. of the slice) over the 128-deep contraction in 32 k-steps.  The contraction is
+// taken in the order in which lane group g's k-step kk is column 32g + kk of M, so each
+// lane reads its row of M as 16-byte runs.  Only S_in is a chain: it stays in LDS from one
+// step to the next (double-buffered), and each step's M and B tiles are loaded into
+// registers during the step before.  Measured at 1 x 16384 x 16 heads (three steps,
+// 64 workgroups): 17.3 us, against 18.3 us for a VALU loop that re-read the state from
+// global memory at every step and 19.4 us for these MFMA tiles without the prefetch.
+// Each step is 1 MFLOP of fp32 MFMA on one CU (about 1.7 us at the fp32 MFMA rate), so
+// the few workgroups, not the loads, now set the time.
 constexpr int COMB_COLS = 32;
 constexpr int COMB_THREADS = 1024;
 __global__ __launch_bounds__(COMB_THREADS) void seg_combine_kernel(PrefillParams p) {
-  __shared__ __attribute__((aligned(16))) float sin_s[D][COMB_COLS];
+  __shared__ __attribute__((aligned(16))) float sbuf[2][D][COMB_COLS];
   const int G = p.seg_G;
   const int slices = D / COMB_COLS;
   const int pair = blockIdx.x / slices;
   const int c0 = (blockIdx.x % slices) * COMB_COLS;
   const int n = pair / p.H, h = pair % p.H;
-  const int tid = threadIdx.x;
-  const int r = tid >> 3;                   // row r
-  const int cq = 4 * (tid & 7);             // columns cq .. cq + 3 of the slice
-  for (int s = 1; s <= G - 2; ++s) {
-    const float* sin = seg_slot(p, n, h, s - 1);
-    const float* M = seg_slot(p, n, h, seg_m_slot(G, s));
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const int rt = wave >> 1, ct = wave & 1;   // output tile: rows 16 rt.., slice columns 16 ct..
+  // lane (r, g) of the tile holds rows 16 rt + 4g + i, column 16 ct + r
+  auto load_mb = [&](int s, float4 (&m)[8], f32x4& bt) {
+    const float* M = seg_slot(p, n, h, seg_m_slot(G, s)) + (16 * rt + r) * D + 32 * g;
     const float* B = seg_slot(p, n, h, seg_b_slot(G, s));
-    float* sout = seg_slot(p, n, h, s);
-    __syncthreads();   // the previous step's reads of sin_s are done
-    for (int e = tid; e < D * COMB_COLS / 4; e += COMB_THREADS) {
-      const int rr = e / (COMB_COLS / 4), c = 4 * (e % (COMB_COLS / 4));
-      *reinterpret_cast<float4*>(&sin_s[rr][c]) =
-          *reinterpret_cast<const float4*>(sin + rr * D + c0 + c);
-    }
-    __syncthreads();
-    const float4 b4 = *reinterpret_cast<const float4*>(B + r * D + c0 + cq);
-    float acc[4] = {b4.x, b4.y, b4.z, b4.w};
-    for (int k = 0; k < D; k += 4) {
-      const float4 m4 = *reinterpret_cast<const float4*>(M + r * D + k);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const float4 x = *reinterpret_cast<const float4*>(&sin_s[k + kk][cq]);
-        const float m = (kk == 0) ? m4.x : (kk == 1) ? m4.y : (kk == 2) ? m4.z : m4.w;
-        acc[0] += m * x.x;
-        acc[1] += m * x.y;
-        acc[2] += m * x.z;
-        acc[3] += m * x.w;
-      }
+    for (int j = 0; j < 8; ++j) m[j] = *reinterpret_cast<const float4*>(M + 4 * j);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bt[i] = B[(16 * rt + 4 * g + i) * D + c0 + 16 * ct + r];
+  };
+  float4 mcur[8];
+  f32x4 bcur;
+  if (G >= 3) load_mb(1, mcur, bcur);
+  {
+    const float* sin = seg_slot(p, n, h, 0);       // S_in(1), from segment 0
+    const int rr = tid >> 3, cc = 4 * (tid & 7);   // 128 rows x 8 float4
+    *reinterpret_cast<float4*>(&sbuf[0][rr][cc]) =
+        *reinterpret_cast<const float4*>(sin + rr * D + c0 + cc);
+  }
+  __syncthreads();
+  for (int s = 1; s <= G - 2; ++s) {
+    float4 mnext[8];
+    f32x4 bnext = bcur;
+    if (s + 1 <= G - 2) load_mb(s + 1, mnext, bnext);
+    const float (*sin)[COMB_COLS] = sbuf[(s - 1) & 1];
+    f32x4 acc = bcur;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float a[4] = {mcur[j].x, mcur[j].y, mcur[j].z, mcur[j].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = mfma_f32(a[e], sin[32 * g + 4 * j + e][16 * ct + r], acc);
     }
-    *reinterpret_cast<float4*>(sout + r * D + c0 + cq) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    // The next step reads this slice of S_in(s+1) back after the barrier at its top.
+    float* sout = seg_slot(p, n, h, s);
+    float (*snext)[COMB_COLS] = sbuf[s & 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sout[(16 * rt + 4 * g + i) * D + c0 + 16 * ct + r] = acc[i];
+      snext[16 * rt + 4 * g + i][16 * ct + r] = acc[i];
+    }
+    __syncthreads();   // S_in(s+1) complete in LDS; S_in(s)'s buffer may be reused
+    if (s + 1 <= G - 2) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mcur[j] = mnext[j];
+      bcur = bnext;
+    }
   }
 }
 
