@@ -153,6 +153,10 @@ EXTRAS_WORKLOAD = (f"commit after {W.VERIFY.name} + conv {W.CONV_PREFILL.name} /
                    f"{W.CONV_UPDATE.name} + gated norm {W.NORM.name} + mixed step {W.MIXED.name}")
 
 
+FULL_WORKLOAD = (f"every configuration: prefill {W.VARLEN.name}, {W.LONG.name}, {W.SINGLE_LONG.name}; "
+                 f"verify {W.VERIFY.name}, {W.VERIFY_B1.name}; next rows")
+
+
 N_XCD = 8           # MI355X: XCDs (GRBM_GUI_ACTIVE is read once per XCD)
 N_SIMD = 256 * 4    # compute units x SIMDs
 
@@ -196,10 +200,15 @@ def summarize(prof_dirs, workload, out_md, mode_flag):
     for cname in ("FETCH_SIZE", "WRITE_SIZE"):
         big = [v for v in calib.get(cname, []) if v * 1024 > 0.5 * CALIB_BYTES]
         factors[cname] = (CALIB_BYTES / 1024) / (sum(big) / len(big)) if big else None
+    full = workload == FULL_WORKLOAD
     lines = [f"# rocprofv3 summary: {workload}", "",
              "Commands (run from /tmp with TMPDIR=/tmp; R = repository root):", "",
              "    rocprofv3 --kernel-trace --stats --output-format csv -d OUT/prof_trace -o trace "
-             f"-- python3 $R/bench.py --no-cpu-baseline {mode_flag}",
+             f"-- python3 $R/bench.py --no-cpu-baseline {mode_flag}".rstrip()]
+    if full:
+        lines += ["    python3 $R/bench.py --summarize OUT/prof_trace --summary-out <this file>", ""]
+    else:
+        lines += [
              "    rocprofv3 --pmc FETCH_SIZE --kernel-trace --output-format csv -d OUT/prof_fetch "
              f"-o fetch -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline {mode_flag} "
              "--calib-copy",
@@ -214,7 +223,8 @@ def summarize(prof_dirs, workload, out_md, mode_flag):
              "--output-format csv -d OUT/prof_lds -o lds -- python3 $R/bench.py --steps 3 "
              f"--warmup 1 --no-cpu-baseline {mode_flag}   (main mode only)",
              "    python3 $R/bench.py --summarize OUT/prof_trace OUT/prof_fetch OUT/prof_write "
-             f"[OUT/prof_mfma OUT/prof_lds] {mode_flag} --summary-out <this file>", "",
+             f"[OUT/prof_mfma OUT/prof_lds] {mode_flag} --summary-out <this file>", ""]
+    lines += [
              "Kernel durations (kernel-trace run only):", "",
              "| kernel | dispatches | avg us | min us | max us |", "|---|---|---|---|---|"]
     def label(key, keys):
@@ -228,20 +238,25 @@ def summarize(prof_dirs, workload, out_md, mode_flag):
     for key, v in sorted(stats.items()):
         lines.append(f"| {label(key, stats)} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | "
                      f"{max(v):.2f} |")
-    lines += ["", "Counter calibration (--calib-copy: an elementwise kernel reading and writing "
-              "1 GiB): bytes = counter KiB x 1024 x factor, with "
-              + ", ".join(f"{c} factor {f:.4f}" if f else f"{c}: not measured"
-                          for c, f in factors.items()), ""]
+    if not full:
+        lines += ["", "Counter calibration (--calib-copy: an elementwise kernel reading and writing "
+                  "1 GiB): bytes = counter KiB x 1024 x factor, with "
+                  + ", ".join(f"{c} factor {f:.4f}" if f else f"{c}: not measured"
+                              for c, f in factors.items()), ""]
     try:
         with open(TRAFFIC_JSON) as f:
             store = json.load(f)
     except (OSError, ValueError):
         store = {}
-    # Entries of workloads this script no longer measures are dropped.
+    # Entries of workloads this script no longer measures are dropped, and so are this
+    # workload's old entries when new counters replace them.
+    have_counters = any("FETCH_SIZE" in cs and "WRITE_SIZE" in cs for cs in counters.values())
     store = {k: v for k, v in store.items()
-             if k.rpartition("@")[2] in (MAIN_WORKLOAD, EXTRAS_WORKLOAD)}
-    lines += ["| kernel | FETCH_SIZE KiB/dispatch (raw) | WRITE_SIZE KiB/dispatch (raw) | "
-              "calibrated HBM MB/dispatch |", "|---|---|---|---|"]
+             if k.rpartition("@")[2] in (MAIN_WORKLOAD, EXTRAS_WORKLOAD)
+             and not (have_counters and k.rpartition("@")[2] == workload)}
+    if not full:
+        lines += ["| kernel | FETCH_SIZE KiB/dispatch (raw) | WRITE_SIZE KiB/dispatch (raw) | "
+                  "calibrated HBM MB/dispatch |", "|---|---|---|---|"]
     for key, cs in sorted(counters.items()):
         k = label(key, counters)
         fr = cs.get("FETCH_SIZE")
@@ -654,10 +669,16 @@ def main():
                     help="measure only the next rows (one JSON line)")
     args = ap.parse_args()
     if args.summarize:
-        extras = args.extras_only
-        summarize(args.summarize, EXTRAS_WORKLOAD if extras else MAIN_WORKLOAD,
-                  args.summary_out or os.path.join(ROOT, "profiles", "summary.md"),
-                  "--extras-only" if extras else "--no-extras")
+        # --extras-only: the next rows; --no-extras: the timed steps and the kernel split;
+        # neither: the full default run (every configuration, kernel trace only).
+        if args.extras_only:
+            wl, flag = EXTRAS_WORKLOAD, "--extras-only"
+        elif args.no_extras:
+            wl, flag = MAIN_WORKLOAD, "--no-extras"
+        else:
+            wl, flag = FULL_WORKLOAD, ""
+        summarize(args.summarize, wl, args.summary_out or os.path.join(ROOT, "profiles", "summary.md"),
+                  flag)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); the library runs the "
