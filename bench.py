@@ -137,13 +137,15 @@ def source_hash(kernel):
 
 
 def stored_traffic(kernel, workload):
-    """Calibrated HBM bytes per launch from the committed counter runs, if still current."""
+    """Calibrated HBM bytes per launch from the committed counter runs, if still current.
+    `kernel` is a summary label: a kernel name, or "name [template args, grid N]" when the
+    run launched it in several forms."""
     try:
         with open(TRAFFIC_JSON) as f:
             rec = json.load(f).get(f"{kernel}@{workload}")
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_hash") != source_hash(kernel):
+    if not rec or rec.get("source_hash") != source_hash(kernel.split(" [")[0]):
         return None
     return rec["fetch_bytes"] + rec["write_bytes"]
 
@@ -503,7 +505,8 @@ def bench_next_rows(iters):
     norm_rows = nx.shape[0] * nx.shape[1]
     norm_bytes = norm_rows * (3 * 2 * D + 4)
     rl_norm = roofline(norm_bytes, 0, t_norm)
-    rl_norm["traffic"] = stored_traffic("kda_gated_rmsnorm", EXTRAS_WORKLOAD)
+    rl_norm["traffic"] = stored_traffic(f"kda_gated_rmsnorm [grid {norm_rows // 32 * 256}]",
+                                        EXTRAS_WORKLOAD)
     del nx, ng, ny, nr
 
     # Short conv on the packed q|k|v columns: prefill at 4 x 8192, update at 64 x 8.
