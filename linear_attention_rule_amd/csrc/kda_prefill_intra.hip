@@ -67,6 +67,12 @@ __device__ __forceinline__ void rec_store(unsigned char* dst, const T16& v) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  const half2v h = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
 // Workgroup barrier for LDS hand-offs only: waits for this wave's LDS operations, not
 // for its global stores (which nothing in the workgroup reads back).
 __device__ __forceinline__ void lds_barrier() {
@@ -90,7 +96,7 @@ __device__ __forceinline__ void load4_bf16(const uint16_t* p, float* dst) {
 // ============================================================================
 
 constexpr int ATS = 68;   // padded row stride (floats) of the 64x64 LDS matrices
-constexpr int KCS = 72;   // padded row stride (halves) of the transposed K_C tile
+constexpr int TMS = 20;   // row stride (floats) of the inverse's 16x16 partial products
 
 struct IntraSmem {
   float AT[64 * ATS];          // A = diag(beta) strict(G), inverted in place into T
@@ -100,8 +106,8 @@ struct IntraSmem {
     // (both factors of an off-diagonal block are <= 1), by (pair(m, w), k-step s, lane)
     half8 R16[6][4][64];
     struct {
-      _Float16 KCt[128 * KCS]; // K_C transposed [channel][token]
-      float tmp[3][256];       // 16x16 partial products of the block inverse
+      uint2 KCs[16 * 2 * 64];  // K_C^T record fragments by (fragment, 8-byte half, lane)
+      float tmp[3][16 * TMS];  // 16x16 partial products of the block inverse, per wave
     } late;
   } u;
   float tot[4][128];           // per-block sums of log2 decay
@@ -114,12 +120,16 @@ struct IntraSmem {
 __device__ __forceinline__ int pair_idx(int m, int w) { return m * (m - 1) / 2 + w; }
 
 // C = X * Y for 16x16 fp32 blocks in LDS (row strides ldx, ldy), accumulated into acc.
+// Lane group k supplies contraction index 4k + kk to step kk, so X is read as one 16-byte
+// row piece per lane.  With row strides of 4 (mod 32) words for X and of 4 (mod 8) words
+// for Y, neither read has bank conflicts (32 banks of 4 bytes).
 __device__ __forceinline__ f32x4 mm16_lds(const float* X, int ldx, const float* Y, int ldy,
                                           f32x4 acc, int lane) {
   const int r = lane & 15, k = lane >> 4;
+  const float4 x4 = *reinterpret_cast<const float4*>(X + r * ldx + 4 * k);
+  const float xv[4] = {x4.x, x4.y, x4.z, x4.w};
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-    acc = mfma_f32(X[r * ldx + 4 * kk + k], Y[(4 * kk + k) * ldy + r], acc);
+  for (int kk = 0; kk < 4; ++kk) acc = mfma_f32(xv[kk], Y[(4 * k + kk) * ldy + r], acc);
   return acc;
 }
 
@@ -133,7 +143,9 @@ __device__ __forceinline__ void store_tile(float* dst, int ld, f32x4 c, int lane
 __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) {
   __shared__ IntraSmem sm;
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, m = lane & 15, g = lane >> 4;
+  // The wave index is uniform; saying so keeps its loops and addressing on the scalar unit.
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, m = lane & 15, g = lane >> 4;
   // Heads fastest: the H workgroups of one chunk slot run together, so their loads
   // cover whole token rows and their records are contiguous.
   const int H = p.H;
@@ -257,10 +269,12 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
   lds_barrier();
   if (tid < 128) __builtin_nontemporal_store(sm.Eb[4][tid], reinterpret_cast<float*>(rec + REC_GAMMA_OFF) + tid);
 
-  // ---- operands.  b = la (in-block cumulative), Lf = 2^b <= 1, Rf = 2^-b >= 1.
-  bf16x8 KL[4], QLh[4], QLl[4], Rh[4], Rl[4];
+  // ---- operands.  b = la (in-block cumulative), Lf = 2^b <= 1, Rf = 2^-b >= 1.  Per
+  // k-step s this also accumulates the diagonal G/P block (bf16 MFMA), publishes the
+  // off-diagonal right factors this wave owns, and turns K_C into K_C^T tiles.
   half8 KL16[4], QL16[4];   // the left factors in fp16, for the off-diagonal blocks
-  _Float16 kch[32];
+  uint2 kct[8];             // K_C^T tiles (channel block 2s + hf), packed fp16 (see below)
+  f32x4 accG = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
   {
     const float rqs = rq * p.scale;
     // Table entries of this thread's 32 channels: 16-byte LDS reads, all issued first.
@@ -276,10 +290,29 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
         ee[0] = e4.x; ee[1] = e4.y; ee[2] = e4.z; ee[3] = e4.w;
         cc[0] = c4.x; cc[1] = c4.y; cc[2] = c4.z; cc[3] = c4.w;
       }
+    // Selector B operands that transpose a 16 x 32 fp16 A tile through the MFMA: column n
+    // of tile hf picks key channel 16 hf + n of the k-step, which lane group n / 4 holds
+    // as element 4 hf + n % 4.  The products are exact (x * 1 plus zeros).
+    half8 sel[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        sel[hf][e] = static_cast<_Float16>(((m >> 2) == g && e == 4 * hf + (m & 3)) ? 1.f : 0.f);
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      half8 kg, qg;
-      float klv[8], qlv[8];
+      // Off-diagonal scale rows 2^(base_mm - base_w) for mm = w+1..3 (clamped in range for
+      // the waves that need fewer; only the needed ones are used).
+      float4 dsc[3][2];
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const int pj = min(pair_idx(min(w + 1 + j, 3), w), 5);
+        dsc[j][0] = *reinterpret_cast<const float4*>(&sm.Dsc[pj][kperm(s, g, 0)]);
+        dsc[j][1] = *reinterpret_cast<const float4*>(&sm.Dsc[pj][kperm(s, g, 4)]);
+      }
+      half8 kg, qg, kc;
+      float klv[8], qlv[8], krv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int i = 8 * s + e;
@@ -291,11 +324,22 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
         const float kr = kh * Rf;             // k^ 2^(base_w - b_t)
         kg[e] = static_cast<_Float16>(-kl * ebv[i]);
         qg[e] = static_cast<_Float16>(ql * ebv[i]);
-        kch[i] = static_cast<_Float16>(kcv[i] * kr);
+        kc[e] = static_cast<_Float16>(kcv[i] * kr);
         klv[e] = kl;
         qlv[e] = ql;
-        kv[i] = kr;  // the fp32 right factor (the diagonal split and the off-diagonal fp16)
+        krv[e] = kr;
       }
+      rec_store(rec + (FR_KG + 4 * w + s) * 1024 + lane * 16, kg);
+      rec_store(rec + (FR_QG + 4 * w + s) * 1024 + lane * 16, qg);
+      // K_C^T: lane (n, g) of tile hf receives channel 32 s + 16 hf + n of tokens
+      // 16 w + 4 g + r, i.e. half (w & 1) of its slot in record fragment (2 s + hf, w / 2).
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const f32x4 t4 = mfma_f16(kc, sel[hf], zero4);
+        kct[2 * s + hf] = make_uint2(pack_f16x2(t4[0], t4[1]), pack_f16x2(t4[2], t4[3]));
+      }
+      // Diagonal block: the right factor reaches 2^115, so bf16 operands; G one product,
+      // P the three-product split.
       u32x4 klp, qhp, qlp, rhp, rlp;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -304,95 +348,84 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
         split_bf16x2(qlv[2 * j], qlv[2 * j + 1], hi, lo);
         qhp[j] = hi;
         qlp[j] = lo;
-        split_bf16x2(kv[8 * s + 2 * j], kv[8 * s + 2 * j + 1], hi, lo);
+        split_bf16x2(krv[2 * j], krv[2 * j + 1], hi, lo);
         rhp[j] = hi;
         rlp[j] = lo;
       }
-      KL[s] = as_bf16x8(klp);
+      accG = mfma_bf16(as_bf16x8(klp), as_bf16x8(rhp), accG);
+      accP = mfma_bf16(as_bf16x8(qhp), as_bf16x8(rhp), accP);
+      accP = mfma_bf16(as_bf16x8(qhp), as_bf16x8(rlp), accP);
+      accP = mfma_bf16(as_bf16x8(qlp), as_bf16x8(rhp), accP);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         KL16[s][e] = static_cast<_Float16>(klv[e]);
         QL16[s][e] = static_cast<_Float16>(qlv[e]);
       }
-      // Off-diagonal right factors, made here by the wave that owns the column block: for
-      // each later row block m, k^ 2^(base_w - b_i) * 2^(base_m - base_w) = k^ 2^(base_m - b_i)
+      // Off-diagonal right factors, made by the wave that owns the column block: for each
+      // later row block mm, k^ 2^(base_w - b_i) * 2^(base_mm - base_w) = k^ 2^(base_mm - b_i)
       // <= 1, rounded to fp16 (its 11-bit mantissa beats bf16; the range is fine).  Wave w
-      // makes 3 - w of them and consumes w, so the waves share the off-diagonal work evenly.
-      for (int mm = w + 1; mm < 4; ++mm) {
-        const float* dsc = sm.Dsc[pair_idx(mm, w)];
-        const float4 d0 = *reinterpret_cast<const float4*>(dsc + kperm(s, g, 0));
-        const float4 d1 = *reinterpret_cast<const float4*>(dsc + kperm(s, g, 4));
-        const float* r = kv + 8 * s;
-        const half8 hr = {static_cast<_Float16>(r[0] * d0.x), static_cast<_Float16>(r[1] * d0.y),
-                          static_cast<_Float16>(r[2] * d0.z), static_cast<_Float16>(r[3] * d0.w),
-                          static_cast<_Float16>(r[4] * d1.x), static_cast<_Float16>(r[5] * d1.y),
-                          static_cast<_Float16>(r[6] * d1.z), static_cast<_Float16>(r[7] * d1.w)};
-        sm.u.R16[pair_idx(mm, w)][s][lane] = hr;
+      // makes 3 - w of them and consumes w.
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        if (j < 3 - w) {
+          const float4 d0 = dsc[j][0], d1 = dsc[j][1];
+          const half8 hr = {static_cast<_Float16>(krv[0] * d0.x), static_cast<_Float16>(krv[1] * d0.y),
+                            static_cast<_Float16>(krv[2] * d0.z), static_cast<_Float16>(krv[3] * d0.w),
+                            static_cast<_Float16>(krv[4] * d1.x), static_cast<_Float16>(krv[5] * d1.y),
+                            static_cast<_Float16>(krv[6] * d1.z), static_cast<_Float16>(krv[7] * d1.w)};
+          sm.u.R16[pair_idx(w + 1 + j, w)][s][lane] = hr;
+        }
       }
-      QLh[s] = as_bf16x8(qhp);
-      QLl[s] = as_bf16x8(qlp);
-      Rh[s] = as_bf16x8(rhp);
-      Rl[s] = as_bf16x8(rlp);
-      rec_store(rec + (FR_KG + 4 * w + s) * 1024 + lane * 16, kg);
-      rec_store(rec + (FR_QG + 4 * w + s) * 1024 + lane * 16, qg);
+    }
+  }
+  // lane (n, g) of a G/P tile holds rows t = 16w + 4g + r, column 16wb + n
+  const float4 b4 = *reinterpret_cast<const float4*>(sm.beta + 16 * w + 4 * g);
+  const float bt[4] = {b4.x, b4.y, b4.z, b4.w};
+  {
+    const int i = 16 * w + m;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tr = 16 * w + 4 * g + r;
+      sm.AT[tr * ATS + i] = (i < tr) ? bt[r] * accG[r] : 0.f;
+      sm.P[tr * ATS + i] = (i <= tr) ? accP[r] : 0.f;   // the left factors carry the scale
     }
   }
   lds_barrier();
 
-  // ---- a2: G and P for row block w, column blocks 0..w (MFMA).  Off the diagonal one
-  // fp16 product each (factors <= 1); on it bf16 (the right factor reaches 2^115): G one
-  // product, P the three-product split.
-  for (int wb = 0; wb <= w; ++wb) {
-    f32x4 accG = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
-    if (wb == w) {
+  // ---- a2, off the diagonal: row block w against column blocks wb < w, one fp16 product
+  // each for G and P (both factors <= 1).  Every right operand is read before any product.
+  {
+    half8 rf[3][4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        accG = mfma_bf16(KL[s], Rh[s], accG);
-        accP = mfma_bf16(QLh[s], Rh[s], accP);
-        accP = mfma_bf16(QLh[s], Rl[s], accP);
-        accP = mfma_bf16(QLl[s], Rh[s], accP);
+    for (int wb = 0; wb < 3; ++wb)
+      if (wb < w) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) rf[wb][s] = sm.u.R16[pair_idx(w, wb)][s][lane];
       }
-    } else {
-      half8 rf[4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) rf[s] = sm.u.R16[pair_idx(w, wb)][s][lane];
+    for (int wb = 0; wb < 3; ++wb)
+      if (wb < w) {
+        f32x4 oG = {0.f, 0.f, 0.f, 0.f}, oP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        accG = mfma_f16(KL16[s], rf[s], accG);
-        accP = mfma_f16(QL16[s], rf[s], accP);
+        for (int s = 0; s < 4; ++s) {
+          oG = mfma_f16(KL16[s], rf[wb][s], oG);
+          oP = mfma_f16(QL16[s], rf[wb][s], oP);
+        }
+        const int i = 16 * wb + m;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tr = 16 * w + 4 * g + r;
+          sm.AT[tr * ATS + i] = bt[r] * oG[r];
+          sm.P[tr * ATS + i] = oP[r];
+        }
       }
-    }
-    // lane (n, g) holds rows t = 16w + 4g + r, column i = 16wb + n
-    const int i = 16 * wb + m;
-    const float4 b4 = *reinterpret_cast<const float4*>(sm.beta + 16 * w + 4 * g);
-    const float bt[4] = {b4.x, b4.y, b4.z, b4.w};
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int tr = 16 * w + 4 * g + r;
-      const float gval = bt[r] * accG[r];
-      const float pval = accP[r];   // the left factors carry the scale
-      sm.AT[tr * ATS + i] = (i < tr) ? gval : 0.f;
-      sm.P[tr * ATS + i] = (i <= tr) ? pval : 0.f;
-    }
-  }
-  // Above the diagonal only blocks (0, 1) and (2, 3) are ever read: the record's 32-deep
-  // k-steps of row blocks 0 and 2 span them.  The inverse reads the lower blocks only.
-  if ((w & 1) == 0) {
-    const int i = 16 * (w + 1) + m;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int tr = 16 * w + 4 * g + r;
-      sm.AT[tr * ATS + i] = 0.f;
-      sm.P[tr * ATS + i] = 0.f;
-    }
   }
   lds_barrier();   // R16 is dead from here on; the union's late view may be written
 
-  // K_C transposed into LDS ([channel][token]) for the K_C^T fragments.
+  // K_C^T halves to their record slots in LDS: [fragment][half][lane], 8 bytes each.
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sm.u.late.KCt[kperm(s, g, e) * KCS + t] = kch[8 * s + e];
+  for (int cb = 0; cb < 8; ++cb)
+    sm.u.late.KCs[((2 * cb + (w >> 1)) * 2 + (w & 1)) * 64 + lane] = kct[cb];
 
   // ---- a3: T = (I + A)^-1.  Diagonal 16x16 blocks by forward substitution (one
   // column per lane, the four lane groups redundant), in place.
@@ -422,64 +455,73 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
     }
   }
   lds_barrier();
-  // Off-diagonal blocks row by row: T_rc = -T_rr * sum_{j=c}^{r-1} A_rj T_jc, computed in
-  // place (A_rc is last needed by T_rc itself; all reads of a row precede its writes).
-  for (int rb = 1; rb < 4; ++rb) {
-    const int cb = w;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (cb < rb) {
-      for (int jb = cb; jb < rb; ++jb)
-        acc = mm16_lds(sm.AT + (16 * rb) * ATS + 16 * jb, ATS, sm.AT + (16 * jb) * ATS + 16 * cb,
-                       ATS, acc, lane);
-      store_tile(sm.u.late.tmp[cb], 16, acc, lane, 1.f);
-    }
-    lds_barrier();
-    if (cb < rb) {
-      f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      z = mm16_lds(sm.AT + (16 * rb) * ATS + 16 * rb, ATS, sm.u.late.tmp[cb], 16, z, lane);
-      store_tile(sm.AT + (16 * rb) * ATS + 16 * cb, ATS, z, lane, -1.f);
-    }
-    lds_barrier();
+  // Off-diagonal blocks by column: wave w makes T_rw = -T_rr sum_{j=w}^{r-1} A_rj T_jw for
+  // r = w+1..3 from the diagonal inverses, the A blocks and its own earlier results.  Each
+  // T_rw goes to the unused upper block (w, r) of the same array, so no A block is
+  // overwritten and no other wave's result is needed: no workgroup barrier until the end.
+  {
+    float* tmp = sm.u.late.tmp[min(w, 2)];
+#pragma unroll
+    for (int rb = 1; rb < 4; ++rb)
+      if (rb > w) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int jb = 0; jb < 3; ++jb)
+          if (jb >= w && jb < rb) {
+            const float* Tjw = (jb == w) ? sm.AT + (16 * w) * ATS + 16 * w
+                                         : sm.AT + (16 * w) * ATS + 16 * jb;
+            acc = mm16_lds(sm.AT + (16 * rb) * ATS + 16 * jb, ATS, Tjw, ATS, acc, lane);
+          }
+        store_tile(tmp, TMS, acc, lane, 1.f);
+        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        z = mm16_lds(sm.AT + (16 * rb) * ATS + 16 * rb, ATS, tmp, TMS, z, lane);
+        store_tile(sm.AT + (16 * w) * ATS + 16 * rb, ATS, z, lane, -1.f);
+      }
   }
+  lds_barrier();
 
-  // ---- record fragments: T' = T diag(beta) and scale*tril(P) (row-major in LDS), K_C^T.
+  // ---- record fragments: T' = T diag(beta) and scale*tril(P), K_C^T.
   // A/B fragment (row block rb, k-step s'): lane (r, g) holds row 16rb + r, columns
-  // kperm(s', g, 0..7).
+  // kperm(s', g, 0..7); the two 4-column halves lie in column blocks 2s' and 2s' + 1.
+  // T_{rb,c} sits at block (rb, rb) on the diagonal and at block (c, rb) below it; blocks
+  // above the diagonal are zero in both matrices.
   {
     const int rb = w;
     for (int sp = 0; sp <= (rb >> 1); ++sp) {
       const int fi = (rb < 2) ? rb : 2 + 2 * (rb - 2) + sp;
-      const int row = 16 * rb + m;
-      const int c0 = kperm(sp, g, 0), c1 = kperm(sp, g, 4);
-      const float4 ta = *reinterpret_cast<const float4*>(sm.AT + row * ATS + c0);
-      const float4 tb = *reinterpret_cast<const float4*>(sm.AT + row * ATS + c1);
-      const float4 ba = *reinterpret_cast<const float4*>(sm.beta + c0);
-      const float4 bb = *reinterpret_cast<const float4*>(sm.beta + c1);
-      half8 tf = {static_cast<_Float16>(ta.x * ba.x), static_cast<_Float16>(ta.y * ba.y),
-                  static_cast<_Float16>(ta.z * ba.z), static_cast<_Float16>(ta.w * ba.w),
-                  static_cast<_Float16>(tb.x * bb.x), static_cast<_Float16>(tb.y * bb.y),
-                  static_cast<_Float16>(tb.z * bb.z), static_cast<_Float16>(tb.w * bb.w)};
+      float tv[8], pv[8];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int cblk = 2 * sp + hf;
+        const int col = kperm(sp, g, 4 * hf);          // 16 cblk + 4 g
+        float4 t4 = make_float4(0.f, 0.f, 0.f, 0.f), p4 = t4;
+        if (cblk <= rb) {
+          const float* src = (cblk == rb) ? sm.AT + (16 * rb + m) * ATS + col
+                                          : sm.AT + (16 * cblk + m) * ATS + 16 * rb + 4 * g;
+          t4 = *reinterpret_cast<const float4*>(src);
+          p4 = *reinterpret_cast<const float4*>(sm.P + (16 * rb + m) * ATS + col);
+        }
+        const float4 bb = *reinterpret_cast<const float4*>(sm.beta + col);
+        tv[4 * hf] = t4.x * bb.x; tv[4 * hf + 1] = t4.y * bb.y;
+        tv[4 * hf + 2] = t4.z * bb.z; tv[4 * hf + 3] = t4.w * bb.w;
+        pv[4 * hf] = p4.x; pv[4 * hf + 1] = p4.y; pv[4 * hf + 2] = p4.z; pv[4 * hf + 3] = p4.w;
+      }
+      half8 tf, pf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        tf[e] = static_cast<_Float16>(tv[e]);
+        pf[e] = static_cast<_Float16>(pv[e]);
+      }
       rec_store(rec + (FR_TP + fi) * 1024 + lane * 16, tf);
-      const float4 pa = *reinterpret_cast<const float4*>(sm.P + row * ATS + c0);
-      const float4 pb = *reinterpret_cast<const float4*>(sm.P + row * ATS + c1);
-      half8 pf = {static_cast<_Float16>(pa.x), static_cast<_Float16>(pa.y),
-                  static_cast<_Float16>(pa.z), static_cast<_Float16>(pa.w),
-                  static_cast<_Float16>(pb.x), static_cast<_Float16>(pb.y),
-                  static_cast<_Float16>(pb.z), static_cast<_Float16>(pb.w)};
       rec_store(rec + (FR_PM + fi) * 1024 + lane * 16, pf);
     }
-    // K_C^T fragments (channel block cb, token k-step s'): lane (r, g) holds channel
-    // 16cb + r, tokens kperm(s', g, 0..7).
+    // K_C^T fragments 4w..4w+3 from the two halves staged by the wave pairs.
 #pragma unroll
-    for (int q2 = 0; q2 < 2; ++q2) {
-      const int cb = 2 * w + q2;
-#pragma unroll
-      for (int sp = 0; sp < 2; ++sp) {
-        const _Float16* src = sm.u.late.KCt + (16 * cb + m) * KCS;
-        const uint2 a = *reinterpret_cast<const uint2*>(src + kperm(sp, g, 0));
-        const uint2 b = *reinterpret_cast<const uint2*>(src + kperm(sp, g, 4));
-        rec_store(rec + (FR_KC + 2 * cb + sp) * 1024 + lane * 16, make_uint4(a.x, a.y, b.x, b.y));
-      }
+    for (int q = 0; q < 4; ++q) {
+      const int f = 4 * w + q;
+      const uint2 a = sm.u.late.KCs[(2 * f) * 64 + lane];
+      const uint2 b = sm.u.late.KCs[(2 * f + 1) * 64 + lane];
+      rec_store(rec + (FR_KC + f) * 1024 + lane * 16, make_uint4(a.x, a.y, b.x, b.y));
     }
   }
 }

@@ -702,7 +702,7 @@ __global__ __launch_bounds__(COMB_THREADS) void seg_combine_kernel(PrefillParams
   const int pair = blockIdx.x / slices;
   const int c0 = (blockIdx.x % slices) * COMB_COLS;
   const int n = pair / p.H, h = pair % p.H;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int r = lane & 15, g = lane >> 4;
   const int rt = wave >> 1, ct = wave & 1;   // output tile: rows 16 rt.., slice columns 16 ct..
   // lane (r, g) of the tile holds rows 16 rt + 4g + i, column 16 ct + r

@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int blk = blockIdx.x;
   const int vt = blk % NVT;
   blk /= NVT;
