@@ -86,6 +86,17 @@ struct VTile {
   static constexpr int COPIES = 64 / ROWS_PER_COPY;
 };
 
+// Bank-conflict-free LDS layouts (32 banks of 4 bytes).  Value tile: in rows 4..7 of
+// every 8 the 16-byte pieces are stored with piece bit 1 flipped, so the compute waves'
+// column reads of rows 4g + r (lane groups g = 0, 1 read together) fall in different
+// banks.  Output tile: the 8-byte piece g of row r is stored at piece g ^ ((r >> 2) & 3),
+// so the 16 rows of one 8-byte write land in all 32 banks.
+__device__ __forceinline__ int vswz(int row) { return 2 * ((row >> 2) & 1); }
+__device__ __forceinline__ int oswz(int row) { return (row >> 2) & 3; }
+// Output tiles are padded by 64 bytes so tiles read side by side by the store wave start
+// 16 banks apart.
+constexpr int OUT_PAD = 32;
+
 // The copies copy wave c of NC issues to bring chunk jj into an LDS buffer: its share
 // of the chunk record (the contiguous 1 KiB fragments [c*PER, (c+1)*PER); all issue the
 // same compile-time count, surplus copies repeating the last fragment with identical
@@ -119,13 +130,16 @@ struct ChunkCopy {
     vlds = lds_ + static_cast<uint32_t>(vt_off + c * VTl::COPIES * 1024);
     lane_off = static_cast<uint32_t>(lane * 16);
     // The value tiles of all compute waves form one [64][16 NB NC] tile (rows of
-    // 32 NB NC bytes); copy wave c issues its instructions c*COPIES .. c*COPIES+COPIES-1,
-    // each 16 bytes per lane, so rows go out as runs of that length.
+    // 32 NB NC bytes, pieces swizzled by vswz); copy wave c issues its instructions
+    // c*COPIES .. c*COPIES+COPIES-1, each 16 bytes per lane, so rows go out as runs of
+    // that length.
     constexpr int LPR = 2 * NB * NC, RPI = 64 / LPR;
+    static_assert(LPR >= 4, "the value-tile swizzle needs four 16-byte pieces per row");
 #pragma unroll
     for (int i = 0; i < VTl::COPIES; ++i) {
-      const int row = min(lane / LPR + RPI * (c * VTl::COPIES + i), Lc - 1);
-      voff[i] = static_cast<uint32_t>((row * p.v_st + 8 * (lane % LPR)) * 2);
+      const int lrow = lane / LPR + RPI * (c * VTl::COPIES + i);   // row in the LDS tile
+      const int row = min(lrow, Lc - 1);
+      voff[i] = static_cast<uint32_t>((row * p.v_st + 8 * ((lane % LPR) ^ vswz(lrow))) * 2);
     }
     f0 = c * PER;
     vrow_lane = static_cast<uint32_t>(min(lane, Lc - 1) * p.v_st * 2);
@@ -198,7 +212,9 @@ __device__ __forceinline__ void store_out_tile(const PrefillParams& p, const uin
   for (int i = 0; i < VTl::COPIES; ++i) {
     const int row = lane / VTl::LANES_PER_ROW + VTl::ROWS_PER_COPY * i;
     const int col = 8 * (lane % VTl::LANES_PER_ROW);
-    const uint4 val = *reinterpret_cast<const uint4*>(so + row * VTl::COLS + col);
+    const int f = oswz(row);
+    uint4 val = *reinterpret_cast<const uint4*>(so + row * VTl::COLS + (col ^ (8 * (f >> 1))));
+    if (f & 1) val = make_uint4(val.z, val.w, val.x, val.y);
     const int64_t orow = p.out_idx ? static_cast<int64_t>(sidx[row]) : tbj + row;
     if (row < Lc && orow >= 0 && orow < p.out_rows)
       *reinterpret_cast<uint4*>(p.out + orow * p.o_st + h * D + v0 + col) = val;
@@ -211,7 +227,7 @@ __device__ __forceinline__ void store_out_tile(const PrefillParams& p, const uin
 // row segments per store instruction than one tile at a time).
 template <int NB, int NW>
 __device__ __forceinline__ void store_out_tiles(const PrefillParams& p,
-                                                const uint16_t (*so)[64 * 16 * NB],
+                                                const uint16_t (*so)[64 * 16 * NB + OUT_PAD],
                                                 const int* sidx, int cs, int ce, int jj, int h,
                                                 int vbase, int lane) {
   constexpr int TCOLS = 16 * NB;                 // columns of one tile
@@ -224,7 +240,9 @@ __device__ __forceinline__ void store_out_tiles(const PrefillParams& p,
 #pragma unroll
   for (int i = 0; i < 64 / RPI; ++i) {
     const int row = lane / LPR + RPI * i;
-    const uint4 val = *reinterpret_cast<const uint4*>(so[tile] + row * TCOLS + tc);
+    const int f = oswz(row);
+    uint4 val = *reinterpret_cast<const uint4*>(so[tile] + row * TCOLS + (tc ^ (8 * (f >> 1))));
+    if (f & 1) val = make_uint4(val.z, val.w, val.x, val.y);
     const int64_t orow = p.out_idx ? static_cast<int64_t>(sidx[row]) : tbj + row;
     if (row < Lc && orow >= 0 && orow < p.out_rows)
       *reinterpret_cast<uint4*>(p.out + orow * p.o_st + h * D + vbase + 8 * q) = val;
@@ -245,13 +263,17 @@ __device__ __forceinline__ void scan_chunk(const unsigned char* __restrict__ R,
   // Stage 1: every LDS read of the X and U products goes out before the first MFMA.
   uint16_t vraw[NB][4][4];
   half8 kgf[16], tpf[6];
+  // Rows 16 tb + 4 g + r have vswz = 2 (g & 1): the swizzled column is one per lane.
+  int vcl[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) vcl[nb] = ((vcol + 16 * nb) ^ (16 * (g & 1))) + nl;
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        vraw[nb][tb][r] = vt[(16 * tb + 4 * g + r) * (16 * NB * NW) + vcol + 16 * nb + nl];
+        vraw[nb][tb][r] = vt[(16 * tb + 4 * g + r) * (16 * NB * NW) + vcl[nb]];
 #pragma unroll
   for (int f = 0; f < 16; ++f) kgf[f] = frag(R, FR_KG + f, lane);
 #pragma unroll
@@ -333,7 +355,8 @@ __device__ __forceinline__ void scan_chunk(const unsigned char* __restrict__ R,
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) o[nb] = mfma_f16(Uf[nb][1], pmf[fi + 1], o[nb]);
       }
-      uint16_t* orow = SO + (16 * tb + nl) * (16 * NB) + 4 * g;
+      // row 16 tb + nl: oswz = (nl >> 2) & 3
+      uint16_t* orow = SO + (16 * tb + nl) * (16 * NB) + 4 * (g ^ ((nl >> 2) & 3));
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
         *reinterpret_cast<uint2*>(orow + 16 * nb) =
@@ -502,7 +525,7 @@ void prefill_scan_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char srec0[BUF_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char srec1[BUF_BYTES];
   __shared__ __attribute__((aligned(16))) uint32_t touch_sink[NC][64];
-  __shared__ __attribute__((aligned(16))) uint16_t sout[2][NW][64 * VTl::COLS];
+  __shared__ __attribute__((aligned(16))) uint16_t sout[2][NW][64 * VTl::COLS + OUT_PAD];
   __shared__ __attribute__((aligned(16))) int sidx[2][64];   // scatter indices of a chunk
   constexpr int BV = 16 * NB * NW;
   constexpr int NVS = D / BV;
