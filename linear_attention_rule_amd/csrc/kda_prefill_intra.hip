@@ -117,6 +117,11 @@ struct IntraSmem {
   float beta[64];
 };
 
+// The prologue's q/k/g staging: 3 tensors x 64 rows x 256 bytes from the start of
+// IntraSmem (A, P and the union are contiguous there and unused until the operands).
+constexpr int STAGE_TENSOR = 64 * 256;
+static_assert(offsetof(IntraSmem, tot) >= 3 * STAGE_TENSOR, "staging overlaps the tables");
+
 __device__ __forceinline__ int pair_idx(int m, int w) { return m * (m - 1) / 2 + w; }
 
 // C = X * Y for 16x16 fp32 blocks in LDS (row strides ldx, ldy), accumulated into acc.
@@ -176,26 +181,51 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
   float qv[32], kv[32], la[32];
   float beta_t;
   {
-    // Every global load of the prologue is issued before the first is used (one
-    // memory round trip instead of the compiler's staggered two or three).
+    // q, k and g rows go through LDS: wave w copies its own 16 token rows of each
+    // (3 x 4 KiB) with 16-byte LDS-DMA loads, four whole rows per instruction, into
+    // space the later phases use (A, P and the union are free until the operands).
+    // Reading them back in the MFMA channel order from registers-sized 8-byte global
+    // loads instead made every load instruction touch 16 rows at 32 bytes each, and
+    // the kernel took 7-10% longer (4x8192 and 8x2048 x16 heads on MI355X).  Pieces
+    // are XOR-swizzled by row (piece p of row r at p ^ (r & 15)) so the read-back of one
+    // channel piece by 16 rows spreads over the banks.
+    unsigned char* stage = reinterpret_cast<unsigned char*>(&sm);
+    const uint32_t stage_lds = lds_addr(stage);
+    const uint16_t* srcs[3] = {p.q, p.k, p.g};
+    const int64_t sts[3] = {p.q_st, p.k_st, p.g_st};
+#pragma unroll
+    for (int x = 0; x < 3; ++x) {
+      const uint64_t base = uniform_addr(srcs[x] + static_cast<int64_t>(t0) * sts[x] + h * D);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 16 * w + 4 * j + (lane >> 4);            // chunk row of this slot
+        const int piece = (lane & 15) ^ (r & 15);              // global piece held here
+        const uint32_t off = static_cast<uint32_t>((min(r, L - 1) * sts[x] + 8 * piece) * 2);
+        lds_dma16(base, off, stage_lds + static_cast<uint32_t>(x * STAGE_TENSOR + (16 * w + 4 * j) * 256));
+      }
+    }
     uint2 qr[8], kr[8], gr[8];
     float4 dr[8];
-    const uint16_t* qp = p.q + tok * p.q_st + h * D;
-    const uint16_t* kp = p.k + tok * p.k_st + h * D;
-    const uint16_t* gp = p.g + tok * p.g_st + h * D;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        dr[2 * s + hh] = *reinterpret_cast<const float4*>(p.dt_bias + h * D + kperm(s, g, 4 * hh));
+    const uint16_t braw = p.beta[tok * p.b_st + h];
+    const float alog = p.A_log[h];
+    // Only this wave's rows are read back, so its own copies are all it waits for.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        const int c0 = kperm(s, g, 4 * hh);
-        qr[2 * s + hh] = *reinterpret_cast<const uint2*>(qp + c0);
-        kr[2 * s + hh] = *reinterpret_cast<const uint2*>(kp + c0);
-        gr[2 * s + hh] = *reinterpret_cast<const uint2*>(gp + c0);
-        dr[2 * s + hh] = *reinterpret_cast<const float4*>(p.dt_bias + h * D + c0);
+        // channels kperm(s, g, 4hh..4hh+3): bytes 64s + 32hh + 8g of the row
+        const int piece = 4 * s + 2 * hh + (g >> 1);
+        const int off = t * 256 + 16 * (piece ^ (t & 15)) + 8 * (g & 1);
+        qr[2 * s + hh] = *reinterpret_cast<const uint2*>(stage + off);
+        kr[2 * s + hh] = *reinterpret_cast<const uint2*>(stage + STAGE_TENSOR + off);
+        gr[2 * s + hh] = *reinterpret_cast<const uint2*>(stage + 2 * STAGE_TENSOR + off);
       }
-    const uint16_t braw = p.beta[tok * p.b_st + h];
-    const float alog = p.A_log[h];
-    asm volatile("" ::: "memory");
     beta_t = vmask * sigmoid_f32(bf16_to_f32(braw));
     float gv[32], dt[32];
 #pragma unroll

@@ -29,40 +29,6 @@ using namespace prefill;
 // before the shared touch-ahead, and 4 took 206-209 against 201-204 us after it).
 constexpr int SCAN_NB = 1;
 
-// 16 bytes per lane from global memory straight into LDS (no VGPR staging):
-// lane l's bytes land at LDS address lds + 16 l.  The global address is a
-// wave-uniform base (SGPR pair) plus a per-lane 32-bit byte offset.  Issued as
-// inline asm so the compiler does not track it: the scan loop orders these copies
-// itself with an explicit s_waitcnt vmcnt and a barrier before any wave reads
-// the buffer.
-__device__ __forceinline__ void lds_dma16(uint64_t gbase, uint32_t lane_off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(lds), "v"(lane_off), "s"(gbase)
-               : "memory", "m0");
-}
-
-// 4 bytes per lane, same addressing (lane l writes lds + 4 l).
-__device__ __forceinline__ void lds_dma4(uint64_t gbase, uint32_t lane_off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
-               :
-               : "s"(lds), "v"(lane_off), "s"(gbase)
-               : "memory", "m0");
-}
-
-__device__ __forceinline__ uint64_t uniform_addr(const void* p) {
-  const uint64_t a = reinterpret_cast<uintptr_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
-  return (static_cast<uint64_t>(hi) << 32) | lo;
-}
-
-// LDS byte address of a __shared__ object (computed once; no per-use cast).
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) unsigned char*)p)));
-}
-
 __device__ __forceinline__ half8 frag(const unsigned char* r, int f, int lane) {
   return *reinterpret_cast<const half8*>(r + f * 1024 + lane * 16);
 }
