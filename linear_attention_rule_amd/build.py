@@ -19,13 +19,10 @@ ARCH = "gfx950"
 SOURCES = ["kda_api.cpp", "kda_verify.hip", "kda_commit.hip", "kda_norm.hip", "kda_conv.hip",
            "kda_prefill_intra.hip", "kda_prefill_scan.hip", "kda_scratch.hip"]
 
-# Per-source additions.  The intra kernel is a chain of short LDS / MFMA phases; the
-# ILP-first scheduler batches each phase's LDS reads ahead of their uses (measured on
-# MI355X: 305 -> 277 us at 4x8192 x16 heads).  The scan kernel keeps the default: there
-# the same scheduler was slower (279 -> 287 us).
-EXTRA_FLAGS = {
-    "kda_prefill_intra.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
-}
+# Per-source additions (none today).  The intra kernel used the ILP-first scheduler while
+# it ran two workgroups per CU; at three (168 VGPRs) the default scheduler fits without
+# spills, and the ILP one cannot allocate registers under that limit.
+EXTRA_FLAGS: dict = {}
 
 # Packed fp32 VALU forms are disabled on purpose: plain fp32 code only.
 HIP_FLAGS = [

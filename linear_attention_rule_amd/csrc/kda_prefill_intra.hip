@@ -68,6 +68,12 @@ __device__ __forceinline__ void rec_store(unsigned char* dst, const T16& v) {
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+// Sum of squares of the two bf16 values packed in x, added to acc.
+__device__ __forceinline__ float sq2_bf16(uint32_t x, float acc) {
+  const bf16x2v v = __builtin_bit_cast(bf16x2v, x);
+  return __builtin_amdgcn_fdot2_f32_bf16(v, v, acc, false);
+}
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
   const half2v h = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
   return __builtin_bit_cast(uint32_t, h);
@@ -98,9 +104,21 @@ __device__ __forceinline__ void load4_bf16(const uint16_t* p, float* dst) {
 constexpr int ATS = 68;   // padded row stride (floats) of the 64x64 LDS matrices
 constexpr int TMS = 20;   // row stride (floats) of the inverse's 16x16 partial products
 
+constexpr int PS = 68;    // row stride (halves) of the fp16 P matrix: conflict-free 8-byte row reads
+
+// 50.25 KiB, so three workgroups share a CU's 160 KiB: the decay tables live in A's space
+// (A is first written after the operands), P is kept in fp16 (the format the record holds),
+// and the block sums sit in the union's tail, past the prologue's staging.
 struct IntraSmem {
-  float AT[64 * ATS];          // A = diag(beta) strict(G), inverted in place into T
-  float P[64 * ATS];           // scale * tril(P)
+  union {
+    float AT[64 * ATS];        // A = diag(beta) strict(G), inverted in place into T
+    struct {                   // decay tables: written after the prologue, dead before A is written
+      float Eb[5][128];        // 2^(base_m), m = 0..4 (base_4 = chunk total)
+      float KCb[4][128];       // 2^(total - base_m)
+      float Dsc[6][128];       // 2^(base_m - base_w), m > w, pair index m*(m-1)/2 + w
+    } tab;
+  } a;
+  _Float16 P[64 * PS];         // scale * tril(P), fp16 (as the record holds it)
   union {
     // fp16 right factors of row blocks w = 0..2 re-referenced to each later row block m
     // (both factors of an off-diagonal block are <= 1), by (pair(m, w), k-step s, lane)
@@ -109,18 +127,20 @@ struct IntraSmem {
       uint2 KCs[16 * 2 * 64];  // K_C^T record fragments by (fragment, 8-byte half, lane)
       float tmp[3][16 * TMS];  // 16x16 partial products of the block inverse, per wave
     } late;
+    struct {
+      unsigned char pad[3 * 64 * 256 - 64 * ATS * 4 - 64 * PS * 2];   // the staged q/k/g
+      float tot[4][128];       // per-block sums of log2 decay (read before the union's other uses)
+    } pre;
   } u;
-  float tot[4][128];           // per-block sums of log2 decay
-  float Eb[5][128];            // 2^(base_m), m = 0..4 (base_4 = chunk total)
-  float KCb[4][128];           // 2^(total - base_m)
-  float Dsc[6][128];           // 2^(base_m - base_w), m > w, pair index m*(m-1)/2 + w
   float beta[64];
 };
 
 // The prologue's q/k/g staging: 3 tensors x 64 rows x 256 bytes from the start of
 // IntraSmem (A, P and the union are contiguous there and unused until the operands).
 constexpr int STAGE_TENSOR = 64 * 256;
-static_assert(offsetof(IntraSmem, tot) >= 3 * STAGE_TENSOR, "staging overlaps the tables");
+static_assert(offsetof(IntraSmem, u) + offsetof(decltype(IntraSmem::u), pre.tot) >= 3 * STAGE_TENSOR,
+              "staging overlaps the block sums");
+static_assert(sizeof(IntraSmem) <= 53 * 1024, "three workgroups per CU");
 
 __device__ __forceinline__ int pair_idx(int m, int w) { return m * (m - 1) / 2 + w; }
 
@@ -145,7 +165,11 @@ __device__ __forceinline__ void store_tile(float* dst, int ld, f32x4 c, int lane
   for (int r = 0; r < 4; ++r) dst[(4 * g + r) * ld + n] = mul * c[r];
 }
 
-__global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) {
+// Three workgroups (12 waves) per CU, 168 VGPRs at most: with two, the kernel was 13-15%
+// slower (4x8192 and 8x2048 x16 heads on MI355X); its phases are latency-bound, and the
+// third workgroup fills the issue slots the other two leave.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void prefill_intra_kernel(PrefillParams p) {
   __shared__ IntraSmem sm;
   const int tid = threadIdx.x;
   // The wave index is uniform; saying so keeps its loops and addressing on the scalar unit.
@@ -178,7 +202,8 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
   const bool valid = t < L;
   const float vmask = valid ? 1.f : 0.f;
   const int64_t tok = static_cast<int64_t>(t0) + min(t, L - 1);
-  float qv[32], kv[32], la[32];
+  uint2 qr[8], kr[8];        // q and k stay packed bf16 until the operands
+  float la[32];
   float beta_t;
   {
     // q, k and g rows go through LDS: wave w copies its own 16 token rows of each
@@ -204,7 +229,7 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
         lds_dma16(base, off, stage_lds + static_cast<uint32_t>(x * STAGE_TENSOR + (16 * w + 4 * j) * 256));
       }
     }
-    uint2 qr[8], kr[8], gr[8];
+    uint2 gr[8];
     float4 dr[8];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -227,33 +252,25 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
         gr[2 * s + hh] = *reinterpret_cast<const uint2*>(stage + 2 * STAGE_TENSOR + off);
       }
     beta_t = vmask * sigmoid_f32(bf16_to_f32(braw));
-    float gv[32], dt[32];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float* qq = qv + 4 * j;
-      float* kk = kv + 4 * j;
-      float* gg = gv + 4 * j;
-      qq[0] = bf16lo_to_f32(qr[j].x); qq[1] = bf16hi_to_f32(qr[j].x);
-      qq[2] = bf16lo_to_f32(qr[j].y); qq[3] = bf16hi_to_f32(qr[j].y);
-      kk[0] = bf16lo_to_f32(kr[j].x); kk[1] = bf16hi_to_f32(kr[j].x);
-      kk[2] = bf16lo_to_f32(kr[j].y); kk[3] = bf16hi_to_f32(kr[j].y);
-      gg[0] = bf16lo_to_f32(gr[j].x); gg[1] = bf16hi_to_f32(gr[j].x);
-      gg[2] = bf16lo_to_f32(gr[j].y); gg[3] = bf16hi_to_f32(gr[j].y);
-      dt[4 * j] = dr[j].x; dt[4 * j + 1] = dr[j].y; dt[4 * j + 2] = dr[j].z; dt[4 * j + 3] = dr[j].w;
-    }
     // log2 decay = lb log2(e) sigmoid(e^A_log (g + dt_bias)), with the exponent's
     // -e^A_log log2(e) folded into one factor.
     const float nEA = -__builtin_amdgcn_exp2f(alog * LOG2E) * LOG2E;
     const float lbm = p.lb_log2e * vmask;
 #pragma unroll
-    for (int i = 0; i < 32; ++i)
-      la[i] = lbm * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f((gv[i] + dt[i]) * nEA));
+    for (int j = 0; j < 8; ++j) {
+      const float gg[4] = {bf16lo_to_f32(gr[j].x), bf16hi_to_f32(gr[j].x),
+                           bf16lo_to_f32(gr[j].y), bf16hi_to_f32(gr[j].y)};
+      const float dd[4] = {dr[j].x, dr[j].y, dr[j].z, dr[j].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        la[4 * j + e] = lbm * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f((gg[e] + dd[e]) * nEA));
+    }
   }
   float ssq = 0.f, ssk = 0.f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    ssq += qv[i] * qv[i];
-    ssk += kv[i] * kv[i];
+  for (int j = 0; j < 8; ++j) {
+    ssq = sq2_bf16(qr[j].x, sq2_bf16(qr[j].y, ssq));
+    ssk = sq2_bf16(kr[j].x, sq2_bf16(kr[j].y, ssk));
   }
   ssq += __shfl_xor(ssq, 16);
   ssq += __shfl_xor(ssq, 32);
@@ -272,7 +289,7 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sm.tot[w][kperm(s, g, e)] = la[8 * s + e];
+      for (int e = 0; e < 8; ++e) sm.u.pre.tot[w][kperm(s, g, e)] = la[8 * s + e];
   }
   lds_barrier();
 
@@ -282,22 +299,22 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
     float base[5];
     base[0] = 0.f;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) base[b + 1] = base[b] + sm.tot[b][c];
+    for (int b = 0; b < 4; ++b) base[b + 1] = base[b] + sm.u.pre.tot[b][c];
     if (part == 0) {
 #pragma unroll
-      for (int b = 0; b < 5; ++b) sm.Eb[b][c] = __builtin_amdgcn_exp2f(base[b]);
+      for (int b = 0; b < 5; ++b) sm.a.tab.Eb[b][c] = __builtin_amdgcn_exp2f(base[b]);
 #pragma unroll
-      for (int b = 0; b < 4; ++b) sm.KCb[b][c] = __builtin_amdgcn_exp2f(base[4] - base[b]);
+      for (int b = 0; b < 4; ++b) sm.a.tab.KCb[b][c] = __builtin_amdgcn_exp2f(base[4] - base[b]);
     } else {
 #pragma unroll
       for (int mm = 1; mm < 4; ++mm)
 #pragma unroll
         for (int ww = 0; ww < mm; ++ww)
-          sm.Dsc[pair_idx(mm, ww)][c] = __builtin_amdgcn_exp2f(base[mm] - base[ww]);
+          sm.a.tab.Dsc[pair_idx(mm, ww)][c] = __builtin_amdgcn_exp2f(base[mm] - base[ww]);
     }
   }
   lds_barrier();
-  if (tid < 128) __builtin_nontemporal_store(sm.Eb[4][tid], reinterpret_cast<float*>(rec + REC_GAMMA_OFF) + tid);
+  if (tid < 128) __builtin_nontemporal_store(sm.a.tab.Eb[4][tid], reinterpret_cast<float*>(rec + REC_GAMMA_OFF) + tid);
 
   // ---- operands.  b = la (in-block cumulative), Lf = 2^b <= 1, Rf = 2^-b >= 1.  Per
   // k-step s this also accumulates the diagonal G/P block (bf16 MFMA), publishes the
@@ -307,19 +324,6 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
   f32x4 accG = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
   {
     const float rqs = rq * p.scale;
-    // Table entries of this thread's 32 channels: 16-byte LDS reads, all issued first.
-    float ebv[32], kcv[32];
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const float4 e4 = *reinterpret_cast<const float4*>(&sm.Eb[w][kperm(s, g, 4 * hh)]);
-        const float4 c4 = *reinterpret_cast<const float4*>(&sm.KCb[w][kperm(s, g, 4 * hh)]);
-        float* ee = ebv + 8 * s + 4 * hh;
-        float* cc = kcv + 8 * s + 4 * hh;
-        ee[0] = e4.x; ee[1] = e4.y; ee[2] = e4.z; ee[3] = e4.w;
-        cc[0] = c4.x; cc[1] = c4.y; cc[2] = c4.z; cc[3] = c4.w;
-      }
     // Selector B operands that transpose a 16 x 32 fp16 A tile through the MFMA: column n
     // of tile hf picks key channel 16 hf + n of the k-step, which lane group n / 4 holds
     // as element 4 hf + n % 4.  The products are exact (x * 1 plus zeros).
@@ -332,14 +336,20 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      // Off-diagonal scale rows 2^(base_mm - base_w) for mm = w+1..3 (clamped in range for
-      // the waves that need fewer; only the needed ones are used).
-      float4 dsc[3][2];
+      // This k-step's table entries and q, k channels (unpacked here to keep registers
+      // for the third workgroup).
+      float ebv[8], kcv[8], qs[8], ks[8];
 #pragma unroll
-      for (int j = 0; j < 3; ++j) {
-        const int pj = min(pair_idx(min(w + 1 + j, 3), w), 5);
-        dsc[j][0] = *reinterpret_cast<const float4*>(&sm.Dsc[pj][kperm(s, g, 0)]);
-        dsc[j][1] = *reinterpret_cast<const float4*>(&sm.Dsc[pj][kperm(s, g, 4)]);
+      for (int hh = 0; hh < 2; ++hh) {
+        const float4 e4 = *reinterpret_cast<const float4*>(&sm.a.tab.Eb[w][kperm(s, g, 4 * hh)]);
+        const float4 c4 = *reinterpret_cast<const float4*>(&sm.a.tab.KCb[w][kperm(s, g, 4 * hh)]);
+        ebv[4 * hh] = e4.x; ebv[4 * hh + 1] = e4.y; ebv[4 * hh + 2] = e4.z; ebv[4 * hh + 3] = e4.w;
+        kcv[4 * hh] = c4.x; kcv[4 * hh + 1] = c4.y; kcv[4 * hh + 2] = c4.z; kcv[4 * hh + 3] = c4.w;
+        const uint2 qw = qr[2 * s + hh], kw = kr[2 * s + hh];
+        qs[4 * hh] = bf16lo_to_f32(qw.x); qs[4 * hh + 1] = bf16hi_to_f32(qw.x);
+        qs[4 * hh + 2] = bf16lo_to_f32(qw.y); qs[4 * hh + 3] = bf16hi_to_f32(qw.y);
+        ks[4 * hh] = bf16lo_to_f32(kw.x); ks[4 * hh + 1] = bf16hi_to_f32(kw.x);
+        ks[4 * hh + 2] = bf16lo_to_f32(kw.y); ks[4 * hh + 3] = bf16hi_to_f32(kw.y);
       }
       half8 kg, qg, kc;
       float klv[8], qlv[8], krv[8];
@@ -348,13 +358,13 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
         const int i = 8 * s + e;
         const float Lf = __builtin_amdgcn_exp2f(la[i]);
         const float Rf = __builtin_amdgcn_exp2f(-la[i]);
-        const float kh = kv[i] * rk;
+        const float kh = ks[e] * rk;
         const float kl = kh * Lf;             // k^ 2^(b_t - base_w)
-        const float ql = qv[i] * rqs * Lf;    // scale q^ 2^(b_t - base_w)
+        const float ql = qs[e] * rqs * Lf;    // scale q^ 2^(b_t - base_w)
         const float kr = kh * Rf;             // k^ 2^(base_w - b_t)
-        kg[e] = static_cast<_Float16>(-kl * ebv[i]);
-        qg[e] = static_cast<_Float16>(ql * ebv[i]);
-        kc[e] = static_cast<_Float16>(kcv[i] * kr);
+        kg[e] = static_cast<_Float16>(-kl * ebv[e]);
+        qg[e] = static_cast<_Float16>(ql * ebv[e]);
+        kc[e] = static_cast<_Float16>(kcv[e] * kr);
         klv[e] = kl;
         qlv[e] = ql;
         krv[e] = kr;
@@ -398,7 +408,9 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
 #pragma unroll
       for (int j = 0; j < 3; ++j) {
         if (j < 3 - w) {
-          const float4 d0 = dsc[j][0], d1 = dsc[j][1];
+          const float* dsc = sm.a.tab.Dsc[pair_idx(w + 1 + j, w)];
+          const float4 d0 = *reinterpret_cast<const float4*>(dsc + kperm(s, g, 0));
+          const float4 d1 = *reinterpret_cast<const float4*>(dsc + kperm(s, g, 4));
           const half8 hr = {static_cast<_Float16>(krv[0] * d0.x), static_cast<_Float16>(krv[1] * d0.y),
                             static_cast<_Float16>(krv[2] * d0.z), static_cast<_Float16>(krv[3] * d0.w),
                             static_cast<_Float16>(krv[4] * d1.x), static_cast<_Float16>(krv[5] * d1.y),
@@ -411,16 +423,16 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
   // lane (n, g) of a G/P tile holds rows t = 16w + 4g + r, column 16wb + n
   const float4 b4 = *reinterpret_cast<const float4*>(sm.beta + 16 * w + 4 * g);
   const float bt[4] = {b4.x, b4.y, b4.z, b4.w};
+  lds_barrier();   // the decay tables are dead from here on; A may be written
   {
     const int i = 16 * w + m;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int tr = 16 * w + 4 * g + r;
-      sm.AT[tr * ATS + i] = (i < tr) ? bt[r] * accG[r] : 0.f;
-      sm.P[tr * ATS + i] = (i <= tr) ? accP[r] : 0.f;   // the left factors carry the scale
+      sm.a.AT[tr * ATS + i] = (i < tr) ? bt[r] * accG[r] : 0.f;
+      sm.P[tr * PS + i] = static_cast<_Float16>((i <= tr) ? accP[r] : 0.f);   // the left factors carry the scale
     }
   }
-  lds_barrier();
 
   // ---- a2, off the diagonal: row block w against column blocks wb < w, one fp16 product
   // each for G and P (both factors <= 1).  Every right operand is read before any product.
@@ -445,8 +457,8 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int tr = 16 * w + 4 * g + r;
-          sm.AT[tr * ATS + i] = bt[r] * oG[r];
-          sm.P[tr * ATS + i] = oP[r];
+          sm.a.AT[tr * ATS + i] = bt[r] * oG[r];
+          sm.P[tr * PS + i] = static_cast<_Float16>(oP[r]);
         }
       }
   }
@@ -462,7 +474,7 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
   {
     const int j = m;
     float x[16];
-    const float* Ab = sm.AT + (16 * w) * ATS + 16 * w;
+    const float* Ab = sm.a.AT + (16 * w) * ATS + 16 * w;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float a[16];
@@ -479,7 +491,7 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
     // All lanes of this wave have read block (w, w) before any lane writes it.
     __builtin_amdgcn_wave_barrier();
     if (g == 0) {
-      float* Tb = sm.AT + (16 * w) * ATS + 16 * w;
+      float* Tb = sm.a.AT + (16 * w) * ATS + 16 * w;
 #pragma unroll
       for (int r = 0; r < 16; ++r) Tb[r * ATS + j] = x[r];
     }
@@ -498,14 +510,14 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
 #pragma unroll
         for (int jb = 0; jb < 3; ++jb)
           if (jb >= w && jb < rb) {
-            const float* Tjw = (jb == w) ? sm.AT + (16 * w) * ATS + 16 * w
-                                         : sm.AT + (16 * w) * ATS + 16 * jb;
-            acc = mm16_lds(sm.AT + (16 * rb) * ATS + 16 * jb, ATS, Tjw, ATS, acc, lane);
+            const float* Tjw = (jb == w) ? sm.a.AT + (16 * w) * ATS + 16 * w
+                                         : sm.a.AT + (16 * w) * ATS + 16 * jb;
+            acc = mm16_lds(sm.a.AT + (16 * rb) * ATS + 16 * jb, ATS, Tjw, ATS, acc, lane);
           }
         store_tile(tmp, TMS, acc, lane, 1.f);
         f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        z = mm16_lds(sm.AT + (16 * rb) * ATS + 16 * rb, ATS, tmp, TMS, z, lane);
-        store_tile(sm.AT + (16 * w) * ATS + 16 * rb, ATS, z, lane, -1.f);
+        z = mm16_lds(sm.a.AT + (16 * rb) * ATS + 16 * rb, ATS, tmp, TMS, z, lane);
+        store_tile(sm.a.AT + (16 * w) * ATS + 16 * rb, ATS, z, lane, -1.f);
       }
   }
   lds_barrier();
@@ -519,29 +531,30 @@ __global__ __launch_bounds__(256, 2) void prefill_intra_kernel(PrefillParams p) 
     const int rb = w;
     for (int sp = 0; sp <= (rb >> 1); ++sp) {
       const int fi = (rb < 2) ? rb : 2 + 2 * (rb - 2) + sp;
-      float tv[8], pv[8];
+      float tv[8];
+      uint32_t pw[4];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         const int cblk = 2 * sp + hf;
         const int col = kperm(sp, g, 4 * hf);          // 16 cblk + 4 g
-        float4 t4 = make_float4(0.f, 0.f, 0.f, 0.f), p4 = t4;
+        float4 t4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        uint2 p2 = make_uint2(0u, 0u);
         if (cblk <= rb) {
-          const float* src = (cblk == rb) ? sm.AT + (16 * rb + m) * ATS + col
-                                          : sm.AT + (16 * cblk + m) * ATS + 16 * rb + 4 * g;
+          const float* src = (cblk == rb) ? sm.a.AT + (16 * rb + m) * ATS + col
+                                          : sm.a.AT + (16 * cblk + m) * ATS + 16 * rb + 4 * g;
           t4 = *reinterpret_cast<const float4*>(src);
-          p4 = *reinterpret_cast<const float4*>(sm.P + (16 * rb + m) * ATS + col);
+          p2 = *reinterpret_cast<const uint2*>(sm.P + (16 * rb + m) * PS + col);
         }
         const float4 bb = *reinterpret_cast<const float4*>(sm.beta + col);
         tv[4 * hf] = t4.x * bb.x; tv[4 * hf + 1] = t4.y * bb.y;
         tv[4 * hf + 2] = t4.z * bb.z; tv[4 * hf + 3] = t4.w * bb.w;
-        pv[4 * hf] = p4.x; pv[4 * hf + 1] = p4.y; pv[4 * hf + 2] = p4.z; pv[4 * hf + 3] = p4.w;
+        pw[2 * hf] = p2.x; pw[2 * hf + 1] = p2.y;
       }
-      half8 tf, pf;
+      half8 tf;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        tf[e] = static_cast<_Float16>(tv[e]);
-        pf[e] = static_cast<_Float16>(pv[e]);
-      }
+      for (int e = 0; e < 8; ++e) tf[e] = static_cast<_Float16>(tv[e]);
+      const u32x4 pwv = {pw[0], pw[1], pw[2], pw[3]};
+      const half8 pf = __builtin_bit_cast(half8, pwv);
       rec_store(rec + (FR_TP + fi) * 1024 + lane * 16, tf);
       rec_store(rec + (FR_PM + fi) * 1024 + lane * 16, pf);
     }
