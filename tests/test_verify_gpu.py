@@ -100,6 +100,19 @@ def test_verify_small_shapes(B, T, H):
     _check(data, out, inter)
 
 
+# (row, head) pair counts on both sides of the launcher's switch from 32-column to
+# 128-column value tiles at 256 pairs, with a padding row.
+@pytest.mark.parametrize("B,H", [(1, 16), (3, 12), (15, 17), (16, 16), (9, 30)])
+def test_verify_both_tile_widths(B, H):
+    case = W.VerifyCase(f"v_tiles_{B}x8_h{H}", B, 8, H, pool_slots=B + 2, seed=2300 + 10 * B + H,
+                        padding_rows=[B - 1] if B > 1 else [])
+    data = W.make_verify(case)
+    d = _dev(data)
+    out, inter = _call(d)
+    torch.cuda.synchronize()
+    _check(data, out, inter)
+
+
 @pytest.mark.parametrize("seed", range(4300, 4306))
 def test_verify_random_shapes(seed):
     """Seeded random shapes: 1-20 rows, 1-16 draft steps (64 at times), 1-6 heads, a few
