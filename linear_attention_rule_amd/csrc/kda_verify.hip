@@ -5,17 +5,35 @@
 // of a row runs in one call, the state starts from the read-only pool and the
 // state after each step is written to its own row of the intermediate buffer.
 //
-// Work split: one workgroup of 256 threads per (row b, head h, value tile).
-// The [128 x BV] fp32 state tile stays in registers for all T steps; thread
-// (rg, cl) owns rows rg*R .. rg*R+R-1 and value columns 4cl .. 4cl+3, so every
-// store of a state row segment is a contiguous BV*4-byte run and a wave writes
-// whole 128-byte lines.  Per step the two key-direction reductions
-// r = S^T k^ and y = S^T q^ share one pass over the decayed state; the output
-// then needs no second pass: o = scale * (y + (k^ . q^) u) with
-// u = beta (v - r), because the update adds k^ u^T.
+// Two forms of the same recurrence (Kimi Linear, the KDA update), chosen by the
+// number of (row, head) pairs:
 //
-// The kernel is bound by the fp32 state writes (T x 64 KiB per (b, h)), so
-// they use non-temporal stores: nothing reads them back in this call.
+// Step form (many pairs, bandwidth-bound; also the fused output norm).  One
+// workgroup of 256 threads per (row b, head h, value tile of BV = 32 or 128 columns):
+// the [128 x BV] fp32 state stays in registers for all T steps; thread (rg, cl) owns
+// rows rg*R .. rg*R+R-1 and value columns 4cl .. 4cl+3, so every store of a state row
+// segment is a contiguous BV*4-byte run and a wave writes whole 128-byte lines.
+// Per step the two key-direction reductions r = S^T k^ and y = S^T q^ share one pass
+// over the decayed state; the output then needs no second pass:
+// o = scale * (y + (k^ . q^) u) with u = beta (v - r), because the update adds k^ u^T.
+//
+// Block form (few pairs, latency-bound).  The step form pays one reduction across
+// the workgroup and one barrier per step.  Over a block of up to 8 steps the same
+// results follow from the state at the block start, S_0 (the WY/UT form of the
+// chunked algorithm on an 8-token chunk):
+//   Gamma_t = prod_{s <= t} alpha_s (per key, within the block),
+//   X_t = S_0^T (Gamma_t . k^_t),  Y_t = S_0^T (Gamma_t . q^_t),
+//   A_ti = sum_j k^_t k^_i Gamma_t / Gamma_i (i < t),
+//   QK_ti = sum_j q^_t k^_i Gamma_t / Gamma_i (i <= t),
+//   u = (I + diag(beta) A)^-1 diag(beta) (v - X),
+//   o_t = scale (Y_t + sum_{i <= t} QK_ti u_i),
+// and then S_t = alpha_t . S_{t-1} + k^_t u_t^T is a purely per-row update.  So a
+// block takes one batch of key-direction sums (all of its steps reduced together)
+// and a tiny 8x8 solve, and the state rows stream out with no cross-lane work
+// between steps.
+//
+// Both forms are bound by the fp32 state writes (T x 64 KiB per (b, h)), so they use
+// non-temporal stores: nothing reads them back in this call.
 #include "kda_internal.h"
 
 namespace kda {
@@ -266,16 +284,377 @@ hipError_t launch_verify_bv(const VerifyParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------------
+// Block form
+
+constexpr int VB = 8;       // draft steps per block
+constexpr int VCOLS = 32;   // value columns per wave
+
+// ---------------------------------------------------------------- cross-lane sums
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int DPP_XOR1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;          // quad_perm [2,3,0,1]
+constexpr int DPP_XOR3 = 0x1B;          // quad_perm [3,2,1,0]
+constexpr int DPP_HALF_MIRROR = 0x141;  // lane ^ 7 within 8
+constexpr int DPP_ROR8 = 0x128;         // lane ^ 8 within 16
+
+__device__ __forceinline__ float xor4(float x) { return dpp<DPP_XOR3>(dpp<DPP_HALF_MIRROR>(x)); }
+
+// Transposing butterfly levels: the first N values of v, halved across one lane bit.
+// A lane with that bit clear keeps values [0, N/2), one with it set keeps [N/2, N), in
+// v[0, N/2); each kept value becomes the sum of its own and the partner lane's copy.
+// The two v_permlane*_swap levels need no selects: swapping v[i] (upper/odd half) with
+// v[i + N/2] (lower/even half) leaves each lane the two copies of its kept value.
+template <int N>
+__device__ __forceinline__ void tlevel5(float* v) {
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]),
+                                                    __float_as_uint(v[i + N / 2]), false, false);
+    v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+}
+template <int N>
+__device__ __forceinline__ void tlevel4(float* v) {
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]),
+                                                    __float_as_uint(v[i + N / 2]), false, false);
+    v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+}
+// Lane bits 3, 2, 1, 0 (DPP within 16-lane rows).
+template <int BIT, int N>
+__device__ __forceinline__ void tlevel_dpp(float* v, int lane) {
+  const bool hi = (lane >> BIT) & 1;
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    const float keep = hi ? v[i + N / 2] : v[i];
+    const float send = hi ? v[i] : v[i + N / 2];
+    float got;
+    if constexpr (BIT == 3) got = dpp<DPP_ROR8>(send);
+    else if constexpr (BIT == 2) got = xor4(send);
+    else if constexpr (BIT == 1) got = dpp<DPP_XOR2>(send);
+    else got = dpp<DPP_XOR1>(send);
+    v[i] = keep + got;
+  }
+}
+__device__ __forceinline__ float sum_bit1(float x) { return x + dpp<DPP_XOR2>(x); }
+__device__ __forceinline__ float sum_bit0(float x) { return x + dpp<DPP_XOR1>(x); }
+
+__device__ __forceinline__ float rl(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
+__device__ __forceinline__ float comp(const float4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// One workgroup of four waves per (row b, head h, 32-column value tile).  Wave wq owns
+// key rows 32wq .. 32wq+31: lane (m, cl) rows 32wq + 4m .. +3 and value columns
+// 4cl .. 4cl+3 (16 fp32 registers), so each store instruction covers 8 rows x 128
+// bytes.  In the block's solve thread (t, c) owns step t of column c.
+__global__ __launch_bounds__(256) void verify_block_kernel(VerifyParams p) {
+  // Per-token tables of the current block.
+  __shared__ __attribute__((aligned(16))) float s_k[VB][D];    // k^
+  __shared__ __attribute__((aligned(16))) float s_a[VB][D];    // alpha
+  __shared__ __attribute__((aligned(16))) float s_kt[VB][D];   // Gamma_t . k^_t
+  __shared__ __attribute__((aligned(16))) float s_qt[VB][D];   // Gamma_t . q^_t
+  __shared__ __attribute__((aligned(16))) float s_kgi[VB][D];  // k^_t / Gamma_t
+  // QK (c <= r) and A_cr (c > r) at 8r + c.
+  __shared__ float s_aq[64];
+  __shared__ float s_beta[VB];
+  // Per-wave partial sums X (0) and Y (1) [wq][x/y][step][col]; v and u [step][col].
+  __shared__ __attribute__((aligned(16))) float s_part[4][2][VB][VCOLS];
+  __shared__ __attribute__((aligned(16))) float s_v[VB][VCOLS];
+  __shared__ __attribute__((aligned(16))) float s_u[VB][VCOLS];
+  __shared__ int s_orow[VB];
+
+  const int T = p.T;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wq = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int vt = blockIdx.x & 3;
+  const int bh = blockIdx.x >> 2;
+  const int h = bh % p.H;
+  const int b = bh / p.H;
+  const int v0 = vt * VCOLS;
+  const int m = lane >> 3;
+  const int cl = lane & 7;
+  const int row0 = 32 * wq + 4 * m;   // this lane's 4 key rows
+  const int st = tid >> 5, sc = tid & 31;   // step and column of this thread's v, u, o
+
+  const int64_t head_elems = static_cast<int64_t>(D) * D;
+  const float scale = p.scale;
+
+  // The block's inputs, loaded one block ahead.  Wave wq: gates of every step (the
+  // cumulative decay needs them all), q and k of steps wq and wq + 4; threads: v of
+  // the solve's (step, column), beta and the output row of step tid.  Steps past nt
+  // repeat the last one (they are zeroed, and nothing of them is stored).
+  uint32_t gw[VB], qw[2], kw[2];
+  uint16_t vb = 0, bb = 0;
+  int orow_l = 0;
+  auto load_block = [&](int t0) {
+    const int nt = min(VB, T - t0);
+    const int64_t tok0 = static_cast<int64_t>(b) * T + t0;
+#pragma unroll
+    for (int i = 0; i < VB; ++i) {
+      const int64_t tok = tok0 + min(i, nt - 1);
+      gw[i] = *reinterpret_cast<const uint32_t*>(p.g + tok * p.g_st + h * D + 2 * lane);
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int64_t tok = tok0 + min(wq + 4 * e, nt - 1);
+      qw[e] = *reinterpret_cast<const uint32_t*>(p.q + tok * p.q_st + h * D + 2 * lane);
+      kw[e] = *reinterpret_cast<const uint32_t*>(p.k + tok * p.k_st + h * D + 2 * lane);
+    }
+    vb = p.v[(tok0 + min(st, nt - 1)) * p.v_st + h * D + v0 + sc];
+    if (tid < nt) {
+      bb = p.beta[(tok0 + tid) * p.b_st + h];
+      orow_l = p.out_idx ? p.out_idx[tok0 + tid] : static_cast<int>(tok0 + tid);
+    }
+  };
+
+  // The slot, the head's constants and the first block's inputs go out together.
+  const int slot = p.idx[b];
+  const float A_log = p.A_log[h];
+  const float2 dtb = *reinterpret_cast<const float2*>(p.dt_bias + h * D + 2 * lane);
+  load_block(0);
+  if (slot < 0 || slot >= p.slots) {
+    // Padding row: zero outputs, no state rows written.
+    for (int e = tid; e < T * VCOLS; e += 256) {
+      const int t = e / VCOLS, c = e % VCOLS;
+      int64_t orow = static_cast<int64_t>(b) * T + t;
+      if (p.out_idx) orow = p.out_idx[orow];
+      if (orow >= 0 && orow < p.out_rows) p.out[orow * p.o_st + h * D + v0 + c] = 0;
+    }
+    return;
+  }
+  // The start state, after the first block's loads so that their wait leaves it in
+  // flight.
+  float4 S[4];
+  {
+    const float* src = p.pool + (static_cast<int64_t>(slot) * p.H + h) * head_elems +
+                       static_cast<int64_t>(row0) * D + v0 + 4 * cl;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) S[j] = *reinterpret_cast<const float4*>(src + j * D);
+  }
+  const float eA = __builtin_amdgcn_exp2f(A_log * LOG2E);
+
+  for (int t0 = 0; t0 < T; t0 += VB) {
+    const int nt = min(VB, T - t0);
+    const int64_t tok0 = static_cast<int64_t>(b) * T + t0;
+    s_v[st][sc] = bf16_to_f32(vb);
+    if (tid < nt) s_orow[tid] = orow_l;
+    if (tid < VB) s_beta[tid] = tid < nt ? sigmoid_f32(bf16_to_f32(bb)) : 0.f;
+
+    // ---------------- norms of steps wq, wq + 4 (lane: keys 2l, 2l+1): four sums, lane
+    // l ends with sum (l >> 4) & 3
+    {
+      float nv[4];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float q0 = bf16lo_to_f32(qw[e]), q1 = bf16hi_to_f32(qw[e]);
+        const float k0 = bf16lo_to_f32(kw[e]), k1 = bf16hi_to_f32(kw[e]);
+        nv[e] = q0 * q0 + q1 * q1;
+        nv[2 + e] = k0 * k0 + k1 * k1;
+      }
+      tlevel5<4>(nv);
+      tlevel4<2>(nv);
+      float nsum = nv[0] + dpp<DPP_ROR8>(nv[0]);
+      nsum += xor4(nsum);
+      nsum = sum_bit0(sum_bit1(nsum));
+
+      // Gates and the in-block cumulative log2 decay b_t <= 0 of every step, then the
+      // table rows of steps wq and wq + 4.  With G_t = 2^(b_t),
+      //   QK_ti = sum_j (G_t q^_t)(k^_i / G_i),  A_ti = sum_j (G_t k^_t)(k^_i / G_i);
+      // the lower bound keeps 1/G below 2^58 over 8 steps.  Uniform conditions are
+      // taken as 0/1 factors and selects: no branches between the transcendentals.
+      float la[VB][2], bc[VB][2];
+      float run0 = 0.f, run1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < VB; ++i) {
+        const float live = i < nt ? p.lb_log2e : 0.f;
+        la[i][0] = live * sigmoid_f32(eA * (bf16lo_to_f32(gw[i]) + dtb.x));
+        la[i][1] = live * sigmoid_f32(eA * (bf16hi_to_f32(gw[i]) + dtb.y));
+        run0 += la[i][0];
+        run1 += la[i][1];
+        bc[i][0] = run0;
+        bc[i][1] = run1;
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int i = wq + 4 * e;
+        float l0 = la[4 * e][0], l1 = la[4 * e][1], r0 = bc[4 * e][0], r1 = bc[4 * e][1];
+#pragma unroll
+        for (int j = 1; j < 4; ++j) {
+          l0 = wq == j ? la[4 * e + j][0] : l0;
+          l1 = wq == j ? la[4 * e + j][1] : l1;
+          r0 = wq == j ? bc[4 * e + j][0] : r0;
+          r1 = wq == j ? bc[4 * e + j][1] : r1;
+        }
+        const float live = i < nt ? 1.f : 0.f;
+        const float rq = live * __builtin_amdgcn_rsqf(rl(nsum, 16 * e) + L2_EPS);
+        const float rk = live * __builtin_amdgcn_rsqf(rl(nsum, 16 * (2 + e)) + L2_EPS);
+        const float k0 = bf16lo_to_f32(kw[e]) * rk, k1 = bf16hi_to_f32(kw[e]) * rk;
+        const float q0 = bf16lo_to_f32(qw[e]) * rq, q1 = bf16hi_to_f32(qw[e]) * rq;
+        const float g0 = __builtin_amdgcn_exp2f(r0), g1 = __builtin_amdgcn_exp2f(r1);
+        const float gi0 = __builtin_amdgcn_exp2f(-r0), gi1 = __builtin_amdgcn_exp2f(-r1);
+        *reinterpret_cast<float2*>(&s_k[i][2 * lane]) = make_float2(k0, k1);
+        *reinterpret_cast<float2*>(&s_a[i][2 * lane]) =
+            make_float2(__builtin_amdgcn_exp2f(l0), __builtin_amdgcn_exp2f(l1));
+        *reinterpret_cast<float2*>(&s_kt[i][2 * lane]) = make_float2(g0 * k0, g1 * k1);
+        *reinterpret_cast<float2*>(&s_qt[i][2 * lane]) = make_float2(g0 * q0, g1 * q1);
+        *reinterpret_cast<float2*>(&s_kgi[i][2 * lane]) = make_float2(gi0 * k0, gi1 * k1);
+      }
+    }
+    __syncthreads();   // the tables, beta and output rows complete
+
+    // ---------------- slots 8r + c of rows r = 2wq, 2wq + 1: QK_rc (c <= r) or A_cr
+    // (c > r); lane l ends with slot 16wq + (l >> 2)
+    {
+      float aq[16];
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        const int r = 2 * wq + rr;
+        const float2 qgr = *reinterpret_cast<const float2*>(&s_qt[r][2 * lane]);
+        const float2 kgir = *reinterpret_cast<const float2*>(&s_kgi[r][2 * lane]);
+#pragma unroll
+        for (int c = 0; c < VB; ++c) {
+          const float2 kgic = *reinterpret_cast<const float2*>(&s_kgi[c][2 * lane]);
+          const float2 kgc = *reinterpret_cast<const float2*>(&s_kt[c][2 * lane]);
+          // both candidates, chosen by a bit mask: no branch on the uniform r (the
+          // candidate not taken can be as large as 2^58, so no arithmetic blend)
+          const float vq = qgr.x * kgic.x + qgr.y * kgic.y;
+          const float va = kgc.x * kgir.x + kgc.y * kgir.y;
+          const uint32_t mq = c <= r ? 0xffffffffu : 0u;
+          aq[8 * rr + c] = __uint_as_float((__float_as_uint(vq) & mq) | (__float_as_uint(va) & ~mq));
+        }
+      }
+      tlevel5<16>(aq);
+      tlevel4<8>(aq);
+      tlevel_dpp<3, 4>(aq, lane);
+      tlevel_dpp<2, 2>(aq, lane);
+      const float av = sum_bit0(sum_bit1(aq[0]));
+      if ((lane & 3) == 0) s_aq[16 * wq + (lane >> 2)] = av;
+    }
+    // ---------------- X and Y: this wave's 32 rows, every step of the block; after the
+    // butterfly lane (m, cl) holds step m, columns 4cl .. 4cl+3.
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const float(*tab)[D] = pass == 0 ? s_kt : s_qt;
+      float acc[4 * VB];
+#pragma unroll
+      for (int t = 0; t < VB; ++t) {
+        const float4 w4 = *reinterpret_cast<const float4*>(&tab[t][row0]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          acc[4 * t + c] = w4.x * comp(S[0], c) + w4.y * comp(S[1], c) + w4.z * comp(S[2], c) +
+                           w4.w * comp(S[3], c);
+      }
+      tlevel5<32>(acc);
+      tlevel4<16>(acc);
+      tlevel_dpp<3, 8>(acc, lane);
+      *reinterpret_cast<float4*>(&s_part[wq][pass][m][4 * cl]) =
+          make_float4(acc[0], acc[1], acc[2], acc[3]);
+    }
+    __syncthreads();   // QK / A and the partial sums complete
+
+    // ---------------- the solve, in thread (t, c): d = v - X for every step of column c,
+    // u by forward substitution of (I + diag(beta) A) u = diag(beta) d (every thread of
+    // the column runs the whole chain and keeps u_t), o_t = scale (Y_t + sum QK_ti u_i).
+    {
+      float u[VB], r[VB];
+#pragma unroll
+      for (int i = 0; i < VB; ++i) {
+        float x = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) x += s_part[q][0][i][sc];
+        r[i] = s_v[i][sc] - x;
+      }
+#pragma unroll
+      for (int i = 0; i < VB; ++i) {
+        u[i] = s_beta[i] * r[i];
+#pragma unroll
+        for (int j = i + 1; j < VB; ++j) r[j] -= s_aq[8 * i + j] * u[i];
+      }
+      float ut = u[0], o = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o += s_part[q][1][st][sc];
+#pragma unroll
+      for (int i = 0; i < VB; ++i) {
+        ut = st == i ? u[i] : ut;
+        const float qk = i <= st ? s_aq[8 * st + i] : 0.f;
+        o += qk * u[i];
+      }
+      s_u[st][sc] = ut;
+      if (st < nt) {
+        const int64_t orow = s_orow[st];
+        if (orow >= 0 && orow < p.out_rows)
+          p.out[orow * p.o_st + h * D + v0 + sc] = static_cast<uint16_t>(pack_bf16x2(o * scale, 0.f));
+      }
+    }
+    __syncthreads();   // u complete
+
+    if (t0 + VB < T) load_block(t0 + VB);   // in flight during the state rows
+
+    // ---------------- the state rows of every step: S_t = alpha_t . S_{t-1} + k^_t u_t^T
+    // (the next step's LDS operands are read one step ahead)
+    float4 u_n = *reinterpret_cast<const float4*>(&s_u[0][4 * cl]);
+    float4 a_n = *reinterpret_cast<const float4*>(&s_a[0][row0]);
+    float4 k_n = *reinterpret_cast<const float4*>(&s_k[0][row0]);
+#pragma unroll
+    for (int t = 0; t < VB; ++t) {
+      const float4 u = u_n, a4 = a_n, k4 = k_n;
+      if (t + 1 < VB) {
+        u_n = *reinterpret_cast<const float4*>(&s_u[t + 1][4 * cl]);
+        a_n = *reinterpret_cast<const float4*>(&s_a[t + 1][row0]);
+        k_n = *reinterpret_cast<const float4*>(&s_k[t + 1][row0]);
+      }
+      if (t >= nt) break;
+      float* dst = p.inter + ((tok0 + t) * p.H + h) * head_elems +
+                   static_cast<int64_t>(row0) * D + v0 + 4 * cl;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float a = comp(a4, j), kk = comp(k4, j);
+        S[j].x = a * S[j].x + kk * u.x;
+        S[j].y = a * S[j].y + kk * u.y;
+        S[j].z = a * S[j].z + kk * u.z;
+        S[j].w = a * S[j].w + kk * u.w;
+        const f32x4 sv = {S[j].x, S[j].y, S[j].z, S[j].w};
+        __builtin_nontemporal_store(sv, reinterpret_cast<f32x4*>(dst + j * D));
+      }
+    }
+    // The block's tables and rows are read before the next block overwrites them.
+    if (t0 + VB < T) __syncthreads();
+  }
+}
+
+hipError_t launch_verify_block(const VerifyParams& p, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(p.B) * p.H * (D / VCOLS));
+  hipLaunchKernelGGL(verify_block_kernel, grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_verify(const VerifyParams& p, hipStream_t s) {
   if (p.B == 0) return hipSuccess;
   // The fused output norm needs whole 128-column rows in one workgroup.
   if (p.out_gate) return launch_verify_bv<128, true>(p, s);
-  // Enough workgroups to cover the 256 compute units: split each head's value
-  // columns four ways when there are few (row, head) pairs.
-  if (static_cast<int64_t>(p.B) * p.H >= 256) return launch_verify_bv<128, false>(p, s);
-  return launch_verify_bv<32, false>(p, s);
+  // Few (row, head) pairs: the block form, a workgroup per 32-column tile (measured on
+  // MI355X at 8 steps and 16 heads: 7.9 against 11.7 us of kernel time at batch 1).  As
+  // the pairs grow the state writes bound the call, and the step form, which
+  // interleaves them with each step's work, keeps the store path busier (per call,
+  // 14.1 against 14.7 us at 96 pairs, 15.2 against 14.9 at 112): 32-column tiles while
+  // there are fewer than 256 pairs, whole 512-byte rows after.
+  const int64_t pairs = static_cast<int64_t>(p.B) * p.H;
+  if (pairs <= 96) return launch_verify_block(p, s);
+  if (pairs < 256) return launch_verify_bv<32, false>(p, s);
+  return launch_verify_bv<128, false>(p, s);
 }
 
 }  // namespace kda

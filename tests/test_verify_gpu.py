@@ -100,10 +100,11 @@ def test_verify_small_shapes(B, T, H):
     _check(data, out, inter)
 
 
-# (row, head) pair counts on both sides of the launcher's switch from 32-column to
-# 128-column value tiles at 256 pairs, with a padding row.
-@pytest.mark.parametrize("B,H", [(1, 16), (3, 12), (15, 17), (16, 16), (9, 30)])
-def test_verify_both_tile_widths(B, H):
+# (row, head) pair counts on both sides of the launcher's switches: the block form up to
+# 96 pairs, the step form with 32-column tiles below 256 and with whole rows from 256
+# on, each with a padding row.
+@pytest.mark.parametrize("B,H", [(1, 16), (3, 12), (6, 16), (7, 14), (15, 17), (16, 16), (9, 30)])
+def test_verify_every_launch_form(B, H):
     case = W.VerifyCase(f"v_tiles_{B}x8_h{H}", B, 8, H, pool_slots=B + 2, seed=2300 + 10 * B + H,
                         padding_rows=[B - 1] if B > 1 else [])
     data = W.make_verify(case)
@@ -171,8 +172,11 @@ def test_verify_strided_fused_projection_inputs():
     assert torch.equal(inter_s, inter_dense)
 
 
-def test_verify_single_steps_match_one_call_bitwise():
-    """T one-step calls, each seeded from the previous call's state row, equal one T-step call."""
+def test_verify_single_steps_match_one_call():
+    """T one-step calls, each seeded from the previous call's state row, agree with one
+    T-step call to fp32 rounding: the multi-step call takes its steps' key-direction sums
+    from the state at the start of each 8-step block, so the sums run in another order.
+    States within 1e-6 relative (L2), outputs within one bf16 step."""
     case = W.VerifyCase("v_steps", 4, 6, 2, pool_slots=8, seed=2103)
     data = W.make_verify(case)
     d = _dev(data)
@@ -185,8 +189,11 @@ def test_verify_single_steps_match_one_call_bitwise():
         dt = dict(d, q=d["q"][rows], k=d["k"][rows], v=d["v"][rows], g=d["g"][rows],
                   beta_logits=d["beta_logits"][rows], state_pool=pool, state_idx=idx, num_steps=1)
         o1, i1 = _call(dt)
-        assert torch.equal(o1, out_all[rows])
-        assert torch.equal(i1[:, 0], inter_all[:, t])
+        a, c = o1.float(), out_all[rows].float()
+        assert torch.all((a - c).abs() <= 2.0 ** -7 * torch.maximum(a.abs(), c.abs()) + 1e-6)
+        for r in range(B):
+            err = TOL.state_rel_l2(i1[r, 0].cpu().numpy(), inter_all[r, t].cpu().numpy())
+            assert err <= 1e-6, (t, r, err)
         pool = i1[:, 0].contiguous()
         idx = torch.arange(B, dtype=torch.int32, device="cuda")
 
