@@ -90,6 +90,26 @@ def test_verify_saturated_and_degenerate_inputs():
     _check(data, out, inter)
 
 
+@pytest.mark.parametrize("B", [2, 40])
+def test_verify_strongest_decay_at_the_lower_bound(B):
+    """Gate logits that saturate the sigmoid at the API's lower bound -5: every step
+    decays by e^-5, so over an 8-step block the block form's 1/Gamma reaches 2^57.7 (its
+    largest value) on the channels where the gate saturates; both launch forms (B = 2:
+    block, B = 40: step) against the oracle."""
+    case = W.VerifyCase(f"v_lb5_{B}", B, 16, 3, pool_slots=B + 2, seed=2500 + B, lower_bound=-5.0)
+    data = W.make_verify(case)
+    n = data["g"].shape[0]
+    t = torch.arange(n)
+    data["g"][t % 3 != 1] = 60.0            # sigmoid -> 1 on every channel
+    data["g"][t % 3 == 1, :, :64] = 60.0    # and on half of them in the other steps
+    print(f"case lb=-5 B {B} T 16 H 3", flush=True)
+    d = _dev(data)
+    out, inter = _call(d)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(inter).all()
+    _check(data, out, inter)
+
+
 @pytest.mark.parametrize("B,T,H", [(3, 1, 1), (5, 3, 2), (2, 16, 3), (1, 64, 2), (40, 8, 8)])
 def test_verify_small_shapes(B, T, H):
     case = W.VerifyCase(f"v_{B}x{T}_h{H}", B, T, H, pool_slots=B + 5, seed=2000 + B * 100 + T + H)
