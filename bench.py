@@ -114,7 +114,7 @@ KERNEL_SOURCES = {
 KERNEL_PATTERNS = {
     "kda_prefill_intra": "prefill_intra_kernel",
     "kda_prefill_scan": "prefill_scan_kernel",
-    "kda_verify": "verify_kernel",
+    "kda_verify": "::verify_",   # the step and the block form
     "kda_commit": "commit_kernel",
     "kda_seg_combine": "seg_combine_kernel",
     "kda_gated_rmsnorm": "gated_rmsnorm_kernel",

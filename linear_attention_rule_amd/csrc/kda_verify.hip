@@ -46,6 +46,9 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// ---------------------------------------------------------------------------------------
+// Step form
+//
 // NORM: the output-gate sigmoid RMSNorm of each output row is applied before the store
 // (SGLang PR #42489, "Modifications": the sigmoid RMSNorm tuned together with the
 // recurrence).  It needs whole rows, so it runs with 128-column tiles only: each step
@@ -53,7 +56,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 // last step groups of 32 threads normalise the rows and store y = o * rstd * weight *
 // sigmoid(gate), with the gate rows staged in the prologue.
 template <int BV, bool NORM>
-__global__ __launch_bounds__(256) void verify_kernel(VerifyParams p) {
+__global__ __launch_bounds__(256) void verify_step_kernel(VerifyParams p) {
   constexpr int NCG = BV / 4;      // column groups (float4) per state row
   constexpr int NRG = 256 / NCG;   // row groups
   constexpr int R = D / NRG;       // rows per thread
@@ -270,17 +273,16 @@ static_assert(sizeof(float) * (64 * (3 * D + D) + 3 * 64 + 2 * 4 * 2 * D) + 16 +
 template <int BV, bool NORM>
 hipError_t launch_verify_bv(const VerifyParams& p, hipStream_t s) {
   const size_t lds = verify_lds_bytes<BV, NORM>(p.T);
-  // The LDS limit for the largest step count is set once per device, not per call
-  // (verify at batch 1 is latency-bound).
+  // The LDS limit for the largest step count is set once per device, not per call.
   static PerDeviceOnce attr_once;
   hipError_t e = attr_once.run([](int, int*) {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(&verify_kernel<BV, NORM>),
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(&verify_step_kernel<BV, NORM>),
                                hipFuncAttributeMaxDynamicSharedMemorySize,
                                static_cast<int>(verify_lds_bytes<BV, NORM>(KDA_MAX_STEPS_INTERNAL)));
   });
   if (e != hipSuccess) return e;
   const dim3 grid(static_cast<unsigned>(p.B) * p.H * (D / BV));
-  hipLaunchKernelGGL((verify_kernel<BV, NORM>), grid, dim3(256), lds, s, p);
+  hipLaunchKernelGGL((verify_step_kernel<BV, NORM>), grid, dim3(256), lds, s, p);
   return hipGetLastError();
 }
 
