@@ -351,15 +351,28 @@ __device__ __forceinline__ float rl(float x, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
 
+// A value that is the same in every lane, moved to a scalar register.
+__device__ __forceinline__ float uniform(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
 __device__ __forceinline__ float comp(const float4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-// One workgroup of four waves per (row b, head h, 32-column value tile).  Wave wq owns
-// key rows 32wq .. 32wq+31: lane (m, cl) rows 32wq + 4m .. +3 and value columns
-// 4cl .. 4cl+3 (16 fp32 registers), so each store instruction covers 8 rows x 128
-// bytes.  In the block's solve thread (t, c) owns step t of column c.
-__global__ __launch_bounds__(256) void verify_block_kernel(VerifyParams p) {
+// One workgroup per (row b, head h) and TILES 32-column value tiles (TILES = 4: the
+// whole head, as the fused output norm needs), four waves per tile.  Wave (tile, wq)
+// owns key rows 32wq .. 32wq+31 of its tile: lane (m, cl) rows 32wq + 4m .. +3 and
+// value columns 4cl .. 4cl+3 (16 fp32 registers), so each store instruction covers 8
+// rows x 128 bytes.  In the block's solve thread (tile, t, c) owns step t of column c.
+//
+// NORM: the output-gate sigmoid RMSNorm of each output row is applied before the store
+// (SGLang PR #42489, "Modifications"): the solve leaves the fp32 output rows in LDS,
+// then groups of 32 threads normalise one row each.
+template <int TILES, bool NORM>
+__global__ __launch_bounds__(256 * TILES) void verify_block_kernel(VerifyParams p) {
+  static_assert(TILES == 1 || TILES == 4, "one tile, or the whole head");
+  static_assert(!NORM || TILES == 4, "the fused norm needs whole rows");
   // Per-token tables of the current block.
   __shared__ __attribute__((aligned(16))) float s_k[VB][D];    // k^
   __shared__ __attribute__((aligned(16))) float s_a[VB][D];    // alpha
@@ -369,32 +382,40 @@ __global__ __launch_bounds__(256) void verify_block_kernel(VerifyParams p) {
   // QK (c <= r) and A_cr (c > r) at 8r + c.
   __shared__ float s_aq[64];
   __shared__ float s_beta[VB];
-  // Per-wave partial sums X (0) and Y (1) [wq][x/y][step][col]; v and u [step][col].
-  __shared__ __attribute__((aligned(16))) float s_part[4][2][VB][VCOLS];
-  __shared__ __attribute__((aligned(16))) float s_v[VB][VCOLS];
-  __shared__ __attribute__((aligned(16))) float s_u[VB][VCOLS];
+  // Per-wave partial sums X (0) and Y (1) [tile][wq][x/y][step][col]; v and u
+  // [step][column of the workgroup].
+  __shared__ __attribute__((aligned(16))) float s_part[TILES][4][2][VB][VCOLS];
+  __shared__ __attribute__((aligned(16))) float s_v[VB][VCOLS * TILES];
+  __shared__ __attribute__((aligned(16))) float s_u[VB][VCOLS * TILES];
   __shared__ int s_orow[VB];
+  // NORM: fp32 output rows and the raw bf16 gate rows of the block.
+  __shared__ __attribute__((aligned(16))) float s_o[NORM ? VB : 1][D];
+  __shared__ __attribute__((aligned(16))) uint16_t s_gate[NORM ? VB : 1][D];
 
   const int T = p.T;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wq = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int vt = blockIdx.x & 3;
-  const int bh = blockIdx.x >> 2;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wq = wave & 3;     // row quarter of the tile
+  const int tile = wave >> 2;  // tile within the workgroup
+  const int vt0 = TILES == 1 ? static_cast<int>(blockIdx.x & 3) : 0;
+  const int bh = TILES == 1 ? static_cast<int>(blockIdx.x >> 2) : static_cast<int>(blockIdx.x);
   const int h = bh % p.H;
   const int b = bh / p.H;
-  const int v0 = vt * VCOLS;
+  const int v0 = (vt0 + tile) * VCOLS;
   const int m = lane >> 3;
   const int cl = lane & 7;
   const int row0 = 32 * wq + 4 * m;   // this lane's 4 key rows
-  const int st = tid >> 5, sc = tid & 31;   // step and column of this thread's v, u, o
+  // step and column of this thread's v, u and o: tile stile, column sc
+  const int stile = tid >> 8, st = (tid >> 5) & 7, sc = tid & 31;
+  const int sv0 = (vt0 + stile) * VCOLS, scol = VCOLS * stile + sc;
 
   const int64_t head_elems = static_cast<int64_t>(D) * D;
   const float scale = p.scale;
 
-  // The block's inputs, loaded one block ahead.  Wave wq: gates of every step (the
-  // cumulative decay needs them all), q and k of steps wq and wq + 4; threads: v of
-  // the solve's (step, column), beta and the output row of step tid.  Steps past nt
+  // The block's inputs, loaded one block ahead.  Wave wq of tile 0: gates of every step
+  // (the cumulative decay needs them all), q and k of steps wq and wq + 4; threads: v
+  // of their (step, column), beta and the output row of step tid.  Steps past nt
   // repeat the last one (they are zeroed, and nothing of them is stored).
   uint32_t gw[VB], qw[2], kw[2];
   uint16_t vb = 0, bb = 0;
@@ -402,18 +423,20 @@ __global__ __launch_bounds__(256) void verify_block_kernel(VerifyParams p) {
   auto load_block = [&](int t0) {
     const int nt = min(VB, T - t0);
     const int64_t tok0 = static_cast<int64_t>(b) * T + t0;
+    if (tile == 0) {
 #pragma unroll
-    for (int i = 0; i < VB; ++i) {
-      const int64_t tok = tok0 + min(i, nt - 1);
-      gw[i] = *reinterpret_cast<const uint32_t*>(p.g + tok * p.g_st + h * D + 2 * lane);
-    }
+      for (int i = 0; i < VB; ++i) {
+        const int64_t tok = tok0 + min(i, nt - 1);
+        gw[i] = *reinterpret_cast<const uint32_t*>(p.g + tok * p.g_st + h * D + 2 * lane);
+      }
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int64_t tok = tok0 + min(wq + 4 * e, nt - 1);
-      qw[e] = *reinterpret_cast<const uint32_t*>(p.q + tok * p.q_st + h * D + 2 * lane);
-      kw[e] = *reinterpret_cast<const uint32_t*>(p.k + tok * p.k_st + h * D + 2 * lane);
+      for (int e = 0; e < 2; ++e) {
+        const int64_t tok = tok0 + min(wq + 4 * e, nt - 1);
+        qw[e] = *reinterpret_cast<const uint32_t*>(p.q + tok * p.q_st + h * D + 2 * lane);
+        kw[e] = *reinterpret_cast<const uint32_t*>(p.k + tok * p.k_st + h * D + 2 * lane);
+      }
     }
-    vb = p.v[(tok0 + min(st, nt - 1)) * p.v_st + h * D + v0 + sc];
+    vb = p.v[(tok0 + min(st, nt - 1)) * p.v_st + h * D + sv0 + sc];
     if (tid < nt) {
       bb = p.beta[(tok0 + tid) * p.b_st + h];
       orow_l = p.out_idx ? p.out_idx[tok0 + tid] : static_cast<int>(tok0 + tid);
@@ -426,12 +449,16 @@ __global__ __launch_bounds__(256) void verify_block_kernel(VerifyParams p) {
   const float2 dtb = *reinterpret_cast<const float2*>(p.dt_bias + h * D + 2 * lane);
   load_block(0);
   if (slot < 0 || slot >= p.slots) {
-    // Padding row: zero outputs, no state rows written.
-    for (int e = tid; e < T * VCOLS; e += 256) {
-      const int t = e / VCOLS, c = e % VCOLS;
+    // Padding row: zero outputs (normalised or not), no state rows written; the norm's
+    // rstd of a zero row is 1/sqrt(eps).
+    for (int e = tid; e < T * VCOLS * TILES; e += 256 * TILES) {
+      const int t = e / (VCOLS * TILES), c = e % (VCOLS * TILES);
       int64_t orow = static_cast<int64_t>(b) * T + t;
       if (p.out_idx) orow = p.out_idx[orow];
-      if (orow >= 0 && orow < p.out_rows) p.out[orow * p.o_st + h * D + v0 + c] = 0;
+      if (orow >= 0 && orow < p.out_rows) {
+        p.out[orow * p.o_st + h * D + vt0 * VCOLS + c] = 0;
+        if (NORM && c == 0 && p.rstd) p.rstd[orow * p.H + h] = __builtin_amdgcn_rsqf(p.norm_eps);
+      }
     }
     return;
   }
@@ -449,99 +476,115 @@ __global__ __launch_bounds__(256) void verify_block_kernel(VerifyParams p) {
   for (int t0 = 0; t0 < T; t0 += VB) {
     const int nt = min(VB, T - t0);
     const int64_t tok0 = static_cast<int64_t>(b) * T + t0;
-    s_v[st][sc] = bf16_to_f32(vb);
+    s_v[st][scol] = bf16_to_f32(vb);
     if (tid < nt) s_orow[tid] = orow_l;
     if (tid < VB) s_beta[tid] = tid < nt ? sigmoid_f32(bf16_to_f32(bb)) : 0.f;
-
-    // ---------------- norms of steps wq, wq + 4 (lane: keys 2l, 2l+1): four sums, lane
-    // l ends with sum (l >> 4) & 3
-    {
-      float nv[4];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const float q0 = bf16lo_to_f32(qw[e]), q1 = bf16hi_to_f32(qw[e]);
-        const float k0 = bf16lo_to_f32(kw[e]), k1 = bf16hi_to_f32(kw[e]);
-        nv[e] = q0 * q0 + q1 * q1;
-        nv[2 + e] = k0 * k0 + k1 * k1;
+    if (NORM && tid < 256) {
+      // The output-gate rows of the block (rows outside the output are never stored;
+      // their gate is not read).
+      const int t = tid >> 5, c4 = 4 * (tid & 31);
+      if (t < nt) {
+        const int64_t orow = p.out_idx ? static_cast<int64_t>(p.out_idx[tok0 + t]) : tok0 + t;
+        uint2 g2 = make_uint2(0, 0);
+        if (orow >= 0 && orow < p.out_rows)
+          g2 = *reinterpret_cast<const uint2*>(p.out_gate + orow * p.og_st + h * D + c4);
+        *reinterpret_cast<uint2*>(&s_gate[t][c4]) = g2;
       }
-      tlevel5<4>(nv);
-      tlevel4<2>(nv);
-      float nsum = nv[0] + dpp<DPP_ROR8>(nv[0]);
-      nsum += xor4(nsum);
-      nsum = sum_bit0(sum_bit1(nsum));
+    }
 
-      // Gates and the in-block cumulative log2 decay b_t <= 0 of every step, then the
-      // table rows of steps wq and wq + 4.  With G_t = 2^(b_t),
-      //   QK_ti = sum_j (G_t q^_t)(k^_i / G_i),  A_ti = sum_j (G_t k^_t)(k^_i / G_i);
-      // the lower bound keeps 1/G below 2^58 over 8 steps.  Uniform conditions are
-      // taken as 0/1 factors and selects: no branches between the transcendentals.
-      float la[VB][2], bc[VB][2];
-      float run0 = 0.f, run1 = 0.f;
-#pragma unroll
-      for (int i = 0; i < VB; ++i) {
-        const float live = i < nt ? p.lb_log2e : 0.f;
-        la[i][0] = live * sigmoid_f32(eA * (bf16lo_to_f32(gw[i]) + dtb.x));
-        la[i][1] = live * sigmoid_f32(eA * (bf16hi_to_f32(gw[i]) + dtb.y));
-        run0 += la[i][0];
-        run1 += la[i][1];
-        bc[i][0] = run0;
-        bc[i][1] = run1;
-      }
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int i = wq + 4 * e;
-        float l0 = la[4 * e][0], l1 = la[4 * e][1], r0 = bc[4 * e][0], r1 = bc[4 * e][1];
-#pragma unroll
-        for (int j = 1; j < 4; ++j) {
-          l0 = wq == j ? la[4 * e + j][0] : l0;
-          l1 = wq == j ? la[4 * e + j][1] : l1;
-          r0 = wq == j ? bc[4 * e + j][0] : r0;
-          r1 = wq == j ? bc[4 * e + j][1] : r1;
+    if (tile == 0) {
+      // ---------------- norms of steps wq, wq + 4 (lane: keys 2l, 2l+1): four sums, lane
+      // l ends with sum (l >> 4) & 3
+      {
+        float nv[4];
+  #pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float q0 = bf16lo_to_f32(qw[e]), q1 = bf16hi_to_f32(qw[e]);
+          const float k0 = bf16lo_to_f32(kw[e]), k1 = bf16hi_to_f32(kw[e]);
+          nv[e] = q0 * q0 + q1 * q1;
+          nv[2 + e] = k0 * k0 + k1 * k1;
         }
-        const float live = i < nt ? 1.f : 0.f;
-        const float rq = live * __builtin_amdgcn_rsqf(rl(nsum, 16 * e) + L2_EPS);
-        const float rk = live * __builtin_amdgcn_rsqf(rl(nsum, 16 * (2 + e)) + L2_EPS);
-        const float k0 = bf16lo_to_f32(kw[e]) * rk, k1 = bf16hi_to_f32(kw[e]) * rk;
-        const float q0 = bf16lo_to_f32(qw[e]) * rq, q1 = bf16hi_to_f32(qw[e]) * rq;
-        const float g0 = __builtin_amdgcn_exp2f(r0), g1 = __builtin_amdgcn_exp2f(r1);
-        const float gi0 = __builtin_amdgcn_exp2f(-r0), gi1 = __builtin_amdgcn_exp2f(-r1);
-        *reinterpret_cast<float2*>(&s_k[i][2 * lane]) = make_float2(k0, k1);
-        *reinterpret_cast<float2*>(&s_a[i][2 * lane]) =
-            make_float2(__builtin_amdgcn_exp2f(l0), __builtin_amdgcn_exp2f(l1));
-        *reinterpret_cast<float2*>(&s_kt[i][2 * lane]) = make_float2(g0 * k0, g1 * k1);
-        *reinterpret_cast<float2*>(&s_qt[i][2 * lane]) = make_float2(g0 * q0, g1 * q1);
-        *reinterpret_cast<float2*>(&s_kgi[i][2 * lane]) = make_float2(gi0 * k0, gi1 * k1);
+        tlevel5<4>(nv);
+        tlevel4<2>(nv);
+        float nsum = nv[0] + dpp<DPP_ROR8>(nv[0]);
+        nsum += xor4(nsum);
+        nsum = sum_bit0(sum_bit1(nsum));
+
+        // Gates and the in-block cumulative log2 decay b_t <= 0 of every step, then the
+        // table rows of steps wq and wq + 4.  With G_t = 2^(b_t),
+        //   QK_ti = sum_j (G_t q^_t)(k^_i / G_i),  A_ti = sum_j (G_t k^_t)(k^_i / G_i);
+        // the lower bound keeps 1/G below 2^58 over 8 steps.  Uniform conditions are
+        // taken as 0/1 factors and selects: no branches between the transcendentals.
+        float la[VB][2], bc[VB][2];
+        float run0 = 0.f, run1 = 0.f;
+  #pragma unroll
+        for (int i = 0; i < VB; ++i) {
+          const float live = i < nt ? p.lb_log2e : 0.f;
+          la[i][0] = live * sigmoid_f32(eA * (bf16lo_to_f32(gw[i]) + dtb.x));
+          la[i][1] = live * sigmoid_f32(eA * (bf16hi_to_f32(gw[i]) + dtb.y));
+          run0 += la[i][0];
+          run1 += la[i][1];
+          bc[i][0] = run0;
+          bc[i][1] = run1;
+        }
+  #pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int i = wq + 4 * e;
+          float l0 = la[4 * e][0], l1 = la[4 * e][1], r0 = bc[4 * e][0], r1 = bc[4 * e][1];
+  #pragma unroll
+          for (int j = 1; j < 4; ++j) {
+            l0 = wq == j ? la[4 * e + j][0] : l0;
+            l1 = wq == j ? la[4 * e + j][1] : l1;
+            r0 = wq == j ? bc[4 * e + j][0] : r0;
+            r1 = wq == j ? bc[4 * e + j][1] : r1;
+          }
+          const float live = i < nt ? 1.f : 0.f;
+          const float rq = live * __builtin_amdgcn_rsqf(rl(nsum, 16 * e) + L2_EPS);
+          const float rk = live * __builtin_amdgcn_rsqf(rl(nsum, 16 * (2 + e)) + L2_EPS);
+          const float k0 = bf16lo_to_f32(kw[e]) * rk, k1 = bf16hi_to_f32(kw[e]) * rk;
+          const float q0 = bf16lo_to_f32(qw[e]) * rq, q1 = bf16hi_to_f32(qw[e]) * rq;
+          const float g0 = __builtin_amdgcn_exp2f(r0), g1 = __builtin_amdgcn_exp2f(r1);
+          const float gi0 = __builtin_amdgcn_exp2f(-r0), gi1 = __builtin_amdgcn_exp2f(-r1);
+          *reinterpret_cast<float2*>(&s_k[i][2 * lane]) = make_float2(k0, k1);
+          *reinterpret_cast<float2*>(&s_a[i][2 * lane]) =
+              make_float2(__builtin_amdgcn_exp2f(l0), __builtin_amdgcn_exp2f(l1));
+          *reinterpret_cast<float2*>(&s_kt[i][2 * lane]) = make_float2(g0 * k0, g1 * k1);
+          *reinterpret_cast<float2*>(&s_qt[i][2 * lane]) = make_float2(g0 * q0, g1 * q1);
+          *reinterpret_cast<float2*>(&s_kgi[i][2 * lane]) = make_float2(gi0 * k0, gi1 * k1);
+        }
       }
     }
     __syncthreads();   // the tables, beta and output rows complete
+    if (tile == 0) {
 
-    // ---------------- slots 8r + c of rows r = 2wq, 2wq + 1: QK_rc (c <= r) or A_cr
-    // (c > r); lane l ends with slot 16wq + (l >> 2)
-    {
-      float aq[16];
-#pragma unroll
-      for (int rr = 0; rr < 2; ++rr) {
-        const int r = 2 * wq + rr;
-        const float2 qgr = *reinterpret_cast<const float2*>(&s_qt[r][2 * lane]);
-        const float2 kgir = *reinterpret_cast<const float2*>(&s_kgi[r][2 * lane]);
-#pragma unroll
-        for (int c = 0; c < VB; ++c) {
-          const float2 kgic = *reinterpret_cast<const float2*>(&s_kgi[c][2 * lane]);
-          const float2 kgc = *reinterpret_cast<const float2*>(&s_kt[c][2 * lane]);
-          // both candidates, chosen by a bit mask: no branch on the uniform r (the
-          // candidate not taken can be as large as 2^58, so no arithmetic blend)
-          const float vq = qgr.x * kgic.x + qgr.y * kgic.y;
-          const float va = kgc.x * kgir.x + kgc.y * kgir.y;
-          const uint32_t mq = c <= r ? 0xffffffffu : 0u;
-          aq[8 * rr + c] = __uint_as_float((__float_as_uint(vq) & mq) | (__float_as_uint(va) & ~mq));
+      // ---------------- slots 8r + c of rows r = 2wq, 2wq + 1: QK_rc (c <= r) or A_cr
+      // (c > r); lane l ends with slot 16wq + (l >> 2)
+      {
+        float aq[16];
+  #pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+          const int r = 2 * wq + rr;
+          const float2 qgr = *reinterpret_cast<const float2*>(&s_qt[r][2 * lane]);
+          const float2 kgir = *reinterpret_cast<const float2*>(&s_kgi[r][2 * lane]);
+  #pragma unroll
+          for (int c = 0; c < VB; ++c) {
+            const float2 kgic = *reinterpret_cast<const float2*>(&s_kgi[c][2 * lane]);
+            const float2 kgc = *reinterpret_cast<const float2*>(&s_kt[c][2 * lane]);
+            // both candidates, chosen by a bit mask: no branch on the uniform r (the
+            // candidate not taken can be as large as 2^58, so no arithmetic blend)
+            const float vq = qgr.x * kgic.x + qgr.y * kgic.y;
+            const float va = kgc.x * kgir.x + kgc.y * kgir.y;
+            const uint32_t mq = c <= r ? 0xffffffffu : 0u;
+            aq[8 * rr + c] = __uint_as_float((__float_as_uint(vq) & mq) | (__float_as_uint(va) & ~mq));
+          }
         }
+        tlevel5<16>(aq);
+        tlevel4<8>(aq);
+        tlevel_dpp<3, 4>(aq, lane);
+        tlevel_dpp<2, 2>(aq, lane);
+        const float av = sum_bit0(sum_bit1(aq[0]));
+        if ((lane & 3) == 0) s_aq[16 * wq + (lane >> 2)] = av;
       }
-      tlevel5<16>(aq);
-      tlevel4<8>(aq);
-      tlevel_dpp<3, 4>(aq, lane);
-      tlevel_dpp<2, 2>(aq, lane);
-      const float av = sum_bit0(sum_bit1(aq[0]));
-      if ((lane & 3) == 0) s_aq[16 * wq + (lane >> 2)] = av;
     }
     // ---------------- X and Y: this wave's 32 rows, every step of the block; after the
     // butterfly lane (m, cl) holds step m, columns 4cl .. 4cl+3.
@@ -560,7 +603,7 @@ __global__ __launch_bounds__(256) void verify_block_kernel(VerifyParams p) {
       tlevel5<32>(acc);
       tlevel4<16>(acc);
       tlevel_dpp<3, 8>(acc, lane);
-      *reinterpret_cast<float4*>(&s_part[wq][pass][m][4 * cl]) =
+      *reinterpret_cast<float4*>(&s_part[tile][wq][pass][m][4 * cl]) =
           make_float4(acc[0], acc[1], acc[2], acc[3]);
     }
     __syncthreads();   // QK / A and the partial sums complete
@@ -574,49 +617,77 @@ __global__ __launch_bounds__(256) void verify_block_kernel(VerifyParams p) {
       for (int i = 0; i < VB; ++i) {
         float x = 0.f;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) x += s_part[q][0][i][sc];
-        r[i] = s_v[i][sc] - x;
+        for (int q = 0; q < 4; ++q) x += s_part[stile][q][0][i][sc];
+        r[i] = s_v[i][scol] - x;
       }
+      // beta and A are the same in every lane: held in scalar registers
 #pragma unroll
       for (int i = 0; i < VB; ++i) {
-        u[i] = s_beta[i] * r[i];
+        u[i] = uniform(s_beta[i]) * r[i];
 #pragma unroll
-        for (int j = i + 1; j < VB; ++j) r[j] -= s_aq[8 * i + j] * u[i];
+        for (int j = i + 1; j < VB; ++j) r[j] -= uniform(s_aq[8 * i + j]) * u[i];
       }
       float ut = u[0], o = 0.f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) o += s_part[q][1][st][sc];
+      for (int q = 0; q < 4; ++q) o += s_part[stile][q][1][st][sc];
 #pragma unroll
       for (int i = 0; i < VB; ++i) {
         ut = st == i ? u[i] : ut;
-        const float qk = i <= st ? s_aq[8 * st + i] : 0.f;
-        o += qk * u[i];
+        const float qa = s_aq[8 * st + i];      // QK_{st,i} for i <= st (A beyond)
+        o += (i <= st ? qa : 0.f) * u[i];
       }
-      s_u[st][sc] = ut;
+      s_u[st][scol] = ut;
       if (st < nt) {
-        const int64_t orow = s_orow[st];
-        if (orow >= 0 && orow < p.out_rows)
-          p.out[orow * p.o_st + h * D + v0 + sc] = static_cast<uint16_t>(pack_bf16x2(o * scale, 0.f));
+        if (NORM) {
+          s_o[st][sv0 + sc] = o * scale;
+        } else {
+          const int64_t orow = s_orow[st];
+          if (orow >= 0 && orow < p.out_rows)
+            p.out[orow * p.o_st + h * D + sv0 + sc] = static_cast<uint16_t>(pack_bf16x2(o * scale, 0.f));
+        }
       }
     }
-    __syncthreads();   // u complete
+    __syncthreads();   // u complete; NORM: the output rows in LDS
+
+    if (NORM && tid < 256) {
+      // groups of 32 threads: one output row each (4 channels per thread)
+      const int t = tid >> 5, c4 = 4 * (tid & 31);
+      if (t < nt) {
+        const float4 o = *reinterpret_cast<const float4*>(&s_o[t][c4]);
+        float ss = o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) ss += __shfl_xor(ss, off);
+        const float rs = __builtin_amdgcn_rsqf(ss * (1.0f / D) + p.norm_eps);
+        const float4 w4 = *reinterpret_cast<const float4*>(p.norm_w + c4);
+        const uint2 gr = *reinterpret_cast<const uint2*>(&s_gate[t][c4]);
+        const float y0 = o.x * rs * w4.x * sigmoid_f32(bf16lo_to_f32(gr.x));
+        const float y1 = o.y * rs * w4.y * sigmoid_f32(bf16hi_to_f32(gr.x));
+        const float y2 = o.z * rs * w4.z * sigmoid_f32(bf16lo_to_f32(gr.y));
+        const float y3 = o.w * rs * w4.w * sigmoid_f32(bf16hi_to_f32(gr.y));
+        const int64_t orow = s_orow[t];
+        if (orow >= 0 && orow < p.out_rows) {
+          *reinterpret_cast<uint2*>(p.out + orow * p.o_st + h * D + c4) =
+              make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
+          if ((tid & 31) == 0 && p.rstd) p.rstd[orow * p.H + h] = rs;
+        }
+      }
+    }
 
     if (t0 + VB < T) load_block(t0 + VB);   // in flight during the state rows
 
     // ---------------- the state rows of every step: S_t = alpha_t . S_{t-1} + k^_t u_t^T
     // (the next step's LDS operands are read one step ahead)
-    float4 u_n = *reinterpret_cast<const float4*>(&s_u[0][4 * cl]);
+    float4 u_n = *reinterpret_cast<const float4*>(&s_u[0][VCOLS * tile + 4 * cl]);
     float4 a_n = *reinterpret_cast<const float4*>(&s_a[0][row0]);
     float4 k_n = *reinterpret_cast<const float4*>(&s_k[0][row0]);
-#pragma unroll
-    for (int t = 0; t < VB; ++t) {
+#pragma unroll 1
+    for (int t = 0; t < nt; ++t) {
       const float4 u = u_n, a4 = a_n, k4 = k_n;
       if (t + 1 < VB) {
-        u_n = *reinterpret_cast<const float4*>(&s_u[t + 1][4 * cl]);
+        u_n = *reinterpret_cast<const float4*>(&s_u[t + 1][VCOLS * tile + 4 * cl]);
         a_n = *reinterpret_cast<const float4*>(&s_a[t + 1][row0]);
         k_n = *reinterpret_cast<const float4*>(&s_k[t + 1][row0]);
       }
-      if (t >= nt) break;
       float* dst = p.inter + ((tok0 + t) * p.H + h) * head_elems +
                    static_cast<int64_t>(row0) * D + v0 + 4 * cl;
 #pragma unroll
@@ -635,9 +706,10 @@ __global__ __launch_bounds__(256) void verify_block_kernel(VerifyParams p) {
   }
 }
 
+template <int TILES, bool NORM>
 hipError_t launch_verify_block(const VerifyParams& p, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(p.B) * p.H * (D / VCOLS));
-  hipLaunchKernelGGL(verify_block_kernel, grid, dim3(256), 0, s, p);
+  const dim3 grid(static_cast<unsigned>(p.B) * p.H * (TILES == 1 ? D / VCOLS : 1));
+  hipLaunchKernelGGL((verify_block_kernel<TILES, NORM>), grid, dim3(256 * TILES), 0, s, p);
   return hipGetLastError();
 }
 
@@ -645,16 +717,22 @@ hipError_t launch_verify_block(const VerifyParams& p, hipStream_t s) {
 
 hipError_t launch_verify(const VerifyParams& p, hipStream_t s) {
   if (p.B == 0) return hipSuccess;
-  // The fused output norm needs whole 128-column rows in one workgroup.
-  if (p.out_gate) return launch_verify_bv<128, true>(p, s);
+  const int64_t pairs = static_cast<int64_t>(p.B) * p.H;
+  if (p.out_gate) {
+    // The fused output norm needs whole 128-column rows in one workgroup: the block
+    // form with the head's four tiles in one workgroup for few pairs (15.2 against
+    // 17.8 us per call at batch 1 of 16 heads, 14.9 against 17.4 at 64 pairs), else
+    // the step form.
+    if (pairs <= 64) return launch_verify_block<4, true>(p, s);
+    return launch_verify_bv<128, true>(p, s);
+  }
   // Few (row, head) pairs: the block form, a workgroup per 32-column tile (measured on
   // MI355X at 8 steps and 16 heads: 7.9 against 11.7 us of kernel time at batch 1).  As
   // the pairs grow the state writes bound the call, and the step form, which
   // interleaves them with each step's work, keeps the store path busier (per call,
   // 14.1 against 14.7 us at 96 pairs, 15.2 against 14.9 at 112): 32-column tiles while
   // there are fewer than 256 pairs, whole 512-byte rows after.
-  const int64_t pairs = static_cast<int64_t>(p.B) * p.H;
-  if (pairs <= 96) return launch_verify_block(p, s);
+  if (pairs <= 96) return launch_verify_block<1, false>(p, s);
   if (pairs < 256) return launch_verify_bv<32, false>(p, s);
   return launch_verify_bv<128, false>(p, s);
 }
