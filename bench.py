@@ -164,9 +164,13 @@ N_SIMD = 256 * 4    # compute units x SIMDs
 
 
 def targs(kernel_name):
-    """Template arguments of a (demangled) kernel name, e.g. '<4, 4, 1, 1>' (or '')."""
-    m = re.search(r"_kernel(<[^()]*>)\(", kernel_name)
-    return m.group(1) if m else ""
+    """Template arguments of a (demangled) kernel name, e.g. '<4, 4, 1, 1>' (or ''), after
+    the verify kernel's form ('step' or 'block')."""
+    m = re.search(r"(\w+)_kernel(<[^()]*>)?\(", kernel_name)
+    if not m:
+        return ""
+    form = m.group(1).split("_")[-1] + " " if m.group(1).startswith("verify_") else ""
+    return (form + (m.group(2) or "")).strip()
 
 
 def summarize(prof_dirs, workload, out_md, mode_flag):
