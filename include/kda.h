@@ -206,6 +206,10 @@ kda_status kda_chunk_prefill_noalloc(const void* q, const void* k, const void* v
  *                   state with every draft token accepted.  Must not overlap the pool.
  *   out             bf16 [B*T, H, 128]
  * B*T above 2^31 - 1 tokens returns KDA_ERR_UNSUPPORTED.
+ * The arithmetic is fp32.  With few (row, head) pairs a call takes its tokens' sums
+ * over the key channels from the state at the start of each block of 8 tokens (the
+ * chunked form on 8 tokens), so a T-token call agrees with T one-token calls to fp32
+ * rounding, not bit for bit; repeated calls are bitwise identical.
  */
 kda_status kda_recurrent_verify(const void* q, const void* k, const void* v, const void* g,
                                 const void* beta_logits, const float* A_log, const float* dt_bias,
