@@ -5,8 +5,8 @@
 // of a row runs in one call, the state starts from the read-only pool and the
 // state after each step is written to its own row of the intermediate buffer.
 //
-// Two forms of the same recurrence (Kimi Linear, the KDA update), chosen by the
-// number of (row, head) pairs:
+// Two forms of the same recurrence (the bounded-gate KDA step of vLLM PR #55737,
+// opening commit message and "Purpose"), chosen by the number of (row, head) pairs:
 //
 // Step form (many pairs, bandwidth-bound; also the fused output norm).  One
 // workgroup of 256 threads per (row b, head h, value tile of BV = 32 or 128 columns):
