@@ -95,8 +95,11 @@ def test_verify_gated_matches_oracle_composition(case):
     print(f"  worst |y - y_ref| / RMS {worst:.2e}", flush=True)
 
 
-def test_verify_gated_padding_scatter_strided_gate_no_rstd():
-    case = W.VerifyCase("gated_small", 6, 5, 3, pool_slots=9, seed=4501, padding_rows=[1, 4])
+# T = 19: three blocks of the block form, the last one partial
+@pytest.mark.parametrize("T", [5, 19])
+def test_verify_gated_padding_scatter_strided_gate_no_rstd(T):
+    case = W.VerifyCase(f"gated_small_t{T}", 6, T, 3, pool_slots=9, seed=4501 + T,
+                        padding_rows=[1, 4])
     data = W.make_verify(case)
     d = _dev(data)
     B, T, H = case.batch, case.steps, case.heads
