@@ -143,11 +143,20 @@ def header_entry_points() -> list[str]:
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # an int: the argtypes (and the descriptors' pointer fields) are c_void_p
+    return None if t is None else t.data_ptr()
+
+
+# torch's current HIP stream of a device as a raw handle; the private accessor skips
+# building a Stream object (a few microseconds per call on the latency-bound verify).
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _stream_handle(device):
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    if _raw_stream is not None:
+        index = device.index if device.index is not None else torch.cuda.current_device()
+        return _raw_stream(index)
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 def _check(status):
@@ -161,21 +170,24 @@ def _token_tensor(name, t, heads, width):
         raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
+    shape = t.shape
     if width is None:
-        if t.dim() != 2 or t.shape[1] != heads:
+        if len(shape) != 2 or shape[1] != heads:
             raise ValueError(f"{name} must be [tokens, {heads}]")
         if t.numel() == 0:
             return 0
-        if t.stride(1) != 1:
+        st = t.stride()
+        if st[1] != 1:
             raise ValueError(f"{name} must have contiguous heads")
     else:
-        if t.dim() != 3 or t.shape[1] != heads or t.shape[2] != width:
+        if len(shape) != 3 or shape[1] != heads or shape[2] != width:
             raise ValueError(f"{name} must be [tokens, {heads}, {width}]")
         if t.numel() == 0:
             return 0
-        if t.stride(2) != 1 or t.stride(1) != width:
+        st = t.stride()
+        if st[2] != 1 or st[1] != width:
             raise ValueError(f"{name} must have dense heads")
-    return t.stride(0)
+    return st[0]
 
 
 def _f32(name, t, shape):
