@@ -729,6 +729,15 @@ def main():
         if ev is not None:
             ev[2].record()
 
+    # The two kernels of the prefill call, each timed as its own call (same arguments).
+    # Measured before the timed steps: the GPU leaves its idle clocks during the first
+    # few milliseconds of sustained work (a step sequence started from idle runs its first
+    # dozen steps 5-10% slower), so the timed steps follow this work rather than the
+    # host-side input generation; the first of these calls get as many untimed ones first.
+    us_intra = median_call_us(lambda: long("intra"), iters, warmup=iters)
+    us_scan = median_call_us(lambda: long("scan"), iters)
+    log(f"split: intra {us_intra:.1f} us  scan {us_scan:.1f} us")
+
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
@@ -748,10 +757,6 @@ def main():
     log(f"timed steps: prefill call {s_prefill * 1e6:.1f} us  verify {s_ver * 1e6:.1f} us "
         f"(medians of {args.steps})")
 
-    # The two kernels of the prefill call, each timed as its own call (same arguments).
-    us_intra = median_call_us(lambda: long("intra"), iters)
-    us_scan = median_call_us(lambda: long("scan"), iters)
-    log(f"split: intra {us_intra:.1f} us  scan {us_scan:.1f} us")
 
     p_bytes, p_flops = long.alg()
     token_heads = T * H
