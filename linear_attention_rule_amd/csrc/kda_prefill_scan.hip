@@ -381,9 +381,18 @@ __device__ __forceinline__ float* seg_slot(const PrefillParams& p, int n, int h,
 __device__ __forceinline__ int seg_m_slot(int G, int s) { return (G - 1) + (s - 1); }
 __device__ __forceinline__ int seg_b_slot(int G, int s) { return (G - 1) + (G - 2) + (s - 1); }
 
-// Chunks [jb, je) of segment s of G over a sequence of nch chunks.
+// Chunks [jb, je) of segment s of G over a sequence of nch chunks.  Segment 0 gets
+// SEG0_WEIGHT / SEG_WEIGHT of a later segment's share: phase A runs it with its outputs
+// on four-wave scans, whose chunk steps take longer than those of the middle segments'
+// state maps beside it (no output products or stores), so a shorter segment 0 ends
+// with them.  Measured at 1 x 16384 x 16 heads (G = 5): prefill call 299 us with equal
+// segments; weights 4, 5, 6, 7 of 8 for segment 0: 287, 284, 279, 288 us.
+constexpr int SEG0_WEIGHT = 3;
+constexpr int SEG_WEIGHT = 4;
 __device__ __forceinline__ int seg_begin(int nch, int G, int s) {
-  return static_cast<int>(static_cast<int64_t>(nch) * s / G);
+  if (s == 0) return 0;
+  return static_cast<int>(static_cast<int64_t>(nch) * (SEG0_WEIGHT + SEG_WEIGHT * (s - 1)) /
+                          (SEG0_WEIGHT + SEG_WEIGHT * (G - 1)));
 }
 
 // MODE_SEQ: whole sequences.  MODE_SEG_A: segment 0 with outputs, and the state maps
