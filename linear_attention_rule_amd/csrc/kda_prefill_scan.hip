@@ -680,44 +680,50 @@ void prefill_scan_kernel(PrefillParams p) {
 
 // Segment start states: S_in(1) comes from segment 0; then, for each middle segment s in
 // order, S_in(s+1) = M_s S_in(s) + B_s, as fp32 MFMA products (v_mfma_f32_16x16x4_f32:
-// fp32 operands, fp32 accumulation).  One workgroup of 16 waves per (sequence, head,
-// 32-column slice); wave w computes the 16x16 output tile (rows 16(w/2).., columns
-// 16(w%2).. of the slice) over the 128-deep contraction in 32 k-steps.  The contraction is
-// taken in the order in which lane group g's k-step kk is column 32g + kk of M, so each
-// lane reads its row of M as 16-byte runs.  Only S_in is a chain: it stays in LDS from one
-// step to the next (double-buffered), and each step's M and B tiles are loaded into
-// registers during the step before.  Measured at 1 x 16384 x 16 heads (three steps,
-// 64 workgroups): 17.3 us, against 18.3 us for a VALU loop that re-read the state from
-// global memory at every step and 19.4 us for these MFMA tiles without the prefetch.
-// Each step is 1 MFLOP of fp32 MFMA on one CU (about 1.7 us at the fp32 MFMA rate), so
-// the few workgroups, not the loads, now set the time.
-constexpr int COMB_COLS = 32;
-constexpr int COMB_THREADS = 1024;
+// fp32 operands, fp32 accumulation).  One workgroup of 8 waves per (sequence, head,
+// 16-column slice); wave w computes the 16x16 output tile of rows 16w.. over the 128-deep
+// contraction in 32 k-steps, so every row of M is loaded by one wave of the workgroup.
+// The contraction is taken in the order in which lane group g's k-step (j, e) is column
+// 16j + 4g + e of M: the four lane groups read each row of M as one 64-byte run.  The
+// eight slices of a pair get workgroup ids congruent mod 8 (one XCD), so they share M in
+// one L2.  Only S_in is a chain: it stays in LDS from one step to the next (double-
+// buffered, rows padded to 20 words so that the two lane groups of a half-wave, four rows
+// apart, read disjoint banks), and each step's M and B tiles are loaded into registers
+// during the step before.  Each step is 1 MFLOP of fp32 MFMA per pair, about 2K cycles
+// on each of its eight CUs.  Measured at 1 x 16384 x 16 heads (three steps, 128
+// workgroups): 10.2 us, against 15-16 us with 32-column slices of 16 waves (64
+// workgroups; 4.4 us per step with the next step's loads, 2.5 us without, bound by the
+// fp32 MFMA rate of one CU), 18.3 us for a VALU loop and 19.4 us for MFMA tiles without
+// the prefetch.
+constexpr int COMB_COLS = 16;
+constexpr int COMB_PAD = 4;
+constexpr int COMB_THREADS = 64 * (D / 16);
 __global__ __launch_bounds__(COMB_THREADS) void seg_combine_kernel(PrefillParams p) {
-  __shared__ __attribute__((aligned(16))) float sbuf[2][D][COMB_COLS];
+  __shared__ __attribute__((aligned(16))) float sbuf[2][D][COMB_COLS + COMB_PAD];
   const int G = p.seg_G;
-  const int slices = D / COMB_COLS;
-  const int pair = blockIdx.x / slices;
-  const int c0 = (blockIdx.x % slices) * COMB_COLS;
+  constexpr int slices = D / COMB_COLS;
+  const int grp = blockIdx.x / (8 * slices), rr8 = blockIdx.x % (8 * slices);
+  const int pair = grp * 8 + (rr8 & 7);
+  if (pair >= p.N * p.H) return;       // the grid is rounded up to whole groups of 8 pairs
+  const int c0 = (rr8 >> 3) * COMB_COLS;
   const int n = pair / p.H, h = pair % p.H;
-  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int tid = threadIdx.x, rt = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int r = lane & 15, g = lane >> 4;
-  const int rt = wave >> 1, ct = wave & 1;   // output tile: rows 16 rt.., slice columns 16 ct..
-  // lane (r, g) of the tile holds rows 16 rt + 4g + i, column 16 ct + r
+  // lane (r, g) of the tile holds rows 16 rt + 4g + i, column r of the slice
   auto load_mb = [&](int s, float4 (&m)[8], f32x4& bt) {
-    const float* M = seg_slot(p, n, h, seg_m_slot(G, s)) + (16 * rt + r) * D + 32 * g;
+    const float* M = seg_slot(p, n, h, seg_m_slot(G, s)) + (16 * rt + r) * D + 4 * g;
     const float* B = seg_slot(p, n, h, seg_b_slot(G, s));
 #pragma unroll
-    for (int j = 0; j < 8; ++j) m[j] = *reinterpret_cast<const float4*>(M + 4 * j);
+    for (int j = 0; j < 8; ++j) m[j] = *reinterpret_cast<const float4*>(M + 16 * j);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) bt[i] = B[(16 * rt + 4 * g + i) * D + c0 + 16 * ct + r];
+    for (int i = 0; i < 4; ++i) bt[i] = B[(16 * rt + 4 * g + i) * D + c0 + r];
   };
   float4 mcur[8];
   f32x4 bcur;
   if (G >= 3) load_mb(1, mcur, bcur);
   {
     const float* sin = seg_slot(p, n, h, 0);       // S_in(1), from segment 0
-    const int rr = tid >> 3, cc = 4 * (tid & 7);   // 128 rows x 8 float4
+    const int rr = tid >> 2, cc = 4 * (tid & 3);   // 128 rows x 4 float4
     *reinterpret_cast<float4*>(&sbuf[0][rr][cc]) =
         *reinterpret_cast<const float4*>(sin + rr * D + c0 + cc);
   }
@@ -726,20 +732,20 @@ __global__ __launch_bounds__(COMB_THREADS) void seg_combine_kernel(PrefillParams
     float4 mnext[8];
     f32x4 bnext = bcur;
     if (s + 1 <= G - 2) load_mb(s + 1, mnext, bnext);
-    const float (*sin)[COMB_COLS] = sbuf[(s - 1) & 1];
+    const float (*sin)[COMB_COLS + COMB_PAD] = sbuf[(s - 1) & 1];
     f32x4 acc = bcur;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float a[4] = {mcur[j].x, mcur[j].y, mcur[j].z, mcur[j].w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc = mfma_f32(a[e], sin[32 * g + 4 * j + e][16 * ct + r], acc);
+      for (int e = 0; e < 4; ++e) acc = mfma_f32(a[e], sin[16 * j + 4 * g + e][r], acc);
     }
     float* sout = seg_slot(p, n, h, s);
-    float (*snext)[COMB_COLS] = sbuf[s & 1];
+    float (*snext)[COMB_COLS + COMB_PAD] = sbuf[s & 1];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sout[(16 * rt + 4 * g + i) * D + c0 + 16 * ct + r] = acc[i];
-      snext[16 * rt + 4 * g + i][16 * ct + r] = acc[i];
+      sout[(16 * rt + 4 * g + i) * D + c0 + r] = acc[i];
+      snext[16 * rt + 4 * g + i][r] = acc[i];
     }
     __syncthreads();   // S_in(s+1) complete in LDS; S_in(s)'s buffer may be reused
     if (s + 1 <= G - 2) {
@@ -797,7 +803,8 @@ hipError_t launch_prefill(const PrefillParams& p_in, int phases, hipStream_t s) 
     // Segment-parallel scan (phase A: segment 0 and the middle segments' state maps;
     // combine; phase C: the later segments from their start states).
     if ((e = launch_scan<4, 4, SCAN_NB, MODE_SEG_A>(p, s)) != hipSuccess) return e;
-    hipLaunchKernelGGL(seg_combine_kernel, dim3(static_cast<unsigned>(pairs * (D / COMB_COLS))),
+    hipLaunchKernelGGL(seg_combine_kernel,
+                       dim3(static_cast<unsigned>(((pairs + 7) / 8) * 8 * (D / COMB_COLS))),
                        dim3(COMB_THREADS), 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return launch_scan<2, 2, SCAN_NB, MODE_SEG_C>(p, s);
