@@ -110,15 +110,29 @@ struct ChunkCopy {
     f0 = c * PER;
     vrow_lane = static_cast<uint32_t>(min(lane, Lc - 1) * p.v_st * 2);
   }
-  __device__ __forceinline__ void all() const {
+  // A scan without outputs (a segment's state map or offset) reads neither scale * Q_Gamma
+  // nor scale * tril(P): it copies the other 39 fragments, spread over its copy waves.
+  static constexpr int NF_NO_OUT = NF - (FR_KC - FR_QG);
+  static constexpr int PER_NO_OUT = (NF_NO_OUT + NC - 1) / NC;
+  __device__ __forceinline__ void all(bool outputs) const {
     if (has_vt) {
 #pragma unroll
       for (int i = 0; i < VTl::COPIES; ++i) lds_dma16(vt, voff[i], vlds + i * 1024u);
     }
+    if (outputs) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const uint32_t f = static_cast<uint32_t>(min(f0 + i, NF - 1));
-      lds_dma16(rec + f * 1024u, lane_off, lds + f * 1024u);
+      for (int i = 0; i < PER; ++i) {
+        const uint32_t f = static_cast<uint32_t>(min(f0 + i, NF - 1));
+        lds_dma16(rec + f * 1024u, lane_off, lds + f * 1024u);
+      }
+    } else {
+      const int k0 = (f0 / PER) * PER_NO_OUT;   // this copy wave's share
+#pragma unroll
+      for (int i = 0; i < PER_NO_OUT; ++i) {
+        const int k = min(k0 + i, NF_NO_OUT - 1);
+        const uint32_t f = static_cast<uint32_t>(k < FR_QG ? k : k + (FR_KC - FR_QG));
+        lds_dma16(rec + f * 1024u, lane_off, lds + f * 1024u);
+      }
     }
   }
   // Pulls this workgroup's share of chunk jj's record into L2 ahead of its copy: the
@@ -569,7 +583,7 @@ void prefill_scan_kernel(PrefillParams p) {
     for (int j = jb; j < je; ++j) {
       const int par = (j - jb) & 1;
       if (j == jb) {
-        CC(p, recbase, cs, ce, jb, h, wk.vs * BV, cw, copy_vt, lane, lds0, vt_off).all();
+        CC(p, recbase, cs, ce, jb, h, wk.vs * BV, cw, copy_vt, lane, lds0, vt_off).all(wk.write_out);
         if (TOUCH) {
           CC(p, recbase, cs, ce, min(jb + 1, je - 1), h, wk.vs * BV, cw, copy_vt, lane, lds1, vt_off)
               .touch(lane, sink, cw, wk.share, wk.nshare, touch_v);
@@ -585,7 +599,7 @@ void prefill_scan_kernel(PrefillParams p) {
       if (wk.write_out && p.out_idx && cw == 0)
         copy_out_index(p, cs, ce, j, lane, lds_addr(sidx[par]));
       if (j + 1 < je) {
-        CC(p, recbase, cs, ce, j + 1, h, wk.vs * BV, cw, copy_vt, lane, par ? lds0 : lds1, vt_off).all();
+        CC(p, recbase, cs, ce, j + 1, h, wk.vs * BV, cw, copy_vt, lane, par ? lds0 : lds1, vt_off).all(wk.write_out);
         if (TOUCH) {
           CC(p, recbase, cs, ce, min(j + 2, je - 1), h, wk.vs * BV, cw, copy_vt, lane, lds0, vt_off)
               .touch(lane, sink, cw, wk.share, wk.nshare, touch_v);
