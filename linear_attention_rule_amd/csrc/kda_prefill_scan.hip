@@ -383,6 +383,7 @@ struct ScanWork {
   const float* start_blk;        // START_WS: the [128][128] start state
   float* fin_blk;                // [128][128] destination of the end state, or null
   bool zero_v, write_out;
+  int active;                    // bit w set: compute wave w scans its value columns
 };
 
 // Workspace of the segment-parallel scan: per (sequence, head), SEG_SLOTS states of
@@ -396,13 +397,14 @@ __device__ __forceinline__ int seg_m_slot(int G, int s) { return (G - 1) + (s - 
 __device__ __forceinline__ int seg_b_slot(int G, int s) { return (G - 1) + (G - 2) + (s - 1); }
 
 // Chunks [jb, je) of segment s of G over a sequence of nch chunks.  Segment 0 gets
-// SEG0_WEIGHT / SEG_WEIGHT of a later segment's share: phase A runs it with its outputs
-// on four-wave scans, whose chunk steps take longer than those of the middle segments'
-// state maps beside it (no output products or stores), so a shorter segment 0 ends
-// with them.  Measured at 1 x 16384 x 16 heads (G = 5): prefill call 299 us with equal
-// segments; weights 4, 5, 6, 7 of 8 for segment 0: 287, 284, 279, 288 us.
-constexpr int SEG0_WEIGHT = 3;
-constexpr int SEG_WEIGHT = 4;
+// SEG0_WEIGHT / SEG_WEIGHT of a later segment's share: phase A runs it with its outputs,
+// whose chunk steps take longer than those of the middle segments' state maps beside it
+// (no output products or stores, 39 of the 61 record fragments), so a shorter segment 0
+// ends with them.  Measured at 1 x 16384 x 16 heads (G = 5, segment 0 on half-active
+// workgroups): prefill call 264, 262, 267, 278, 287 us for weights 4, 5, 6, 7, 8 of 8;
+// with segment 0 on full four-wave workgroups, 287, 284, 279, 288, 299 us.
+constexpr int SEG0_WEIGHT = 5;
+constexpr int SEG_WEIGHT = 8;
 __device__ __forceinline__ int seg_begin(int nch, int G, int s) {
   if (s == 0) return 0;
   return static_cast<int>(static_cast<int64_t>(nch) * (SEG0_WEIGHT + SEG_WEIGHT * (s - 1)) /
@@ -419,7 +421,7 @@ constexpr int MODE_SEG_C = 2;
 // Workgroups per unit of work (a pair, or a pair's segment) and the workgroup -> unit
 // order: ids are dealt round-robin to the 8 XCDs (id % 8), so the workgroups of one
 // unit get ids congruent mod 8 and share one L2 for the records they all read.
-template <int MODE, int NVS>
+template <int MODE, int NVS, int NW>
 __device__ __forceinline__ bool decode_work(const PrefillParams& p, ScanWork& wk) {
   constexpr int PER_UNIT = (MODE == MODE_SEG_A) ? 2 * NVS : NVS;
   const int H = p.H;
@@ -439,6 +441,7 @@ __device__ __forceinline__ bool decode_work(const PrefillParams& p, ScanWork& wk
   wk.start_blk = nullptr;
   wk.zero_v = false;
   wk.write_out = true;
+  wk.active = (1 << NW) - 1;
   wk.share = cg;
   wk.nshare = NVS;
   if (MODE == MODE_SEQ) {
@@ -455,8 +458,12 @@ __device__ __forceinline__ bool decode_work(const PrefillParams& p, ScanWork& wk
     wk.jb = seg_begin(nch, G, s);
     wk.je = seg_begin(nch, G, s + 1);
     if (s == 0) {
-      if (cg >= NVS) return false;
-      wk.vs = cg;
+      // Segment 0 carries the outputs: its 2 NVS workgroups each run half of their
+      // compute waves, so each CU reads the record once per 32 value columns, as the
+      // two-compute-wave scans do (the chunk step of a full four-wave scan with outputs
+      // is longer than that of the maps beside it).
+      wk.vs = cg >> 1;
+      wk.active = ((1 << (NW / 2)) - 1) << ((cg & 1) * (NW / 2));
       wk.start = START_INIT;
       wk.fin_blk = seg_slot(p, wk.n, wk.h, 0);          // S_in(1)
       return true;
@@ -510,6 +517,8 @@ __attribute__((amdgpu_waves_per_eu((NW + NC + store_waves<NW>() + 3) / 4,
 void prefill_scan_kernel(PrefillParams p) {
   using VTl = VTile<NB>;
   static_assert(NC == NW, "each copy wave fills its share of the combined value tile");
+  static_assert(MODE != MODE_SEG_A || store_waves<NW>() == 0,
+                "segment 0's half-active workgroups have their copy waves store the outputs");
   constexpr int BUF_BYTES = REC_BYTES + NW * VTl::BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char srec0[BUF_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char srec1[BUF_BYTES];
@@ -519,7 +528,7 @@ void prefill_scan_kernel(PrefillParams p) {
   constexpr int BV = 16 * NB * NW;
   constexpr int NVS = D / BV;
   ScanWork wk;
-  if (!decode_work<MODE, NVS>(p, wk)) return;   // uniform: the whole workgroup exits
+  if (!decode_work<MODE, NVS, NW>(p, wk)) return;   // uniform: the whole workgroup exits
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   constexpr bool STORE_WAVE = store_waves<NW>() == 1;
@@ -577,7 +586,7 @@ void prefill_scan_kernel(PrefillParams p) {
     // One wave touches each 128-byte line of value rows: the two 64-byte halves of a
     // line belong to value slices 2k and 2k+1, and a workgroup's copy waves share it.
     const bool touch_v = copy_vt && cw == 0 && (wk.vs & 1) == 0;
-    const bool store = has_vt && wk.write_out;
+    const bool store = has_vt && wk.write_out && ((wk.active >> w) & 1);
     const uint32_t lds0 = lds_addr(srec0), lds1 = lds_addr(srec1);
     const uint32_t sink = lds_addr(touch_sink[cw]);
     for (int j = jb; j < je; ++j) {
@@ -623,9 +632,11 @@ void prefill_scan_kernel(PrefillParams p) {
     return;
   }
 
-  // Start state: S[nb][cb][r] = S[16cb + 4g + r][v0 + 16nb + nl].
+  // Start state: S[nb][cb][r] = S[16cb + 4g + r][v0 + 16nb + nl].  An inactive compute
+  // wave keeps the workgroup's barrier count and does nothing else.
+  const bool act = (wk.active >> w) & 1;
   f32x4 S[NB][8];
-  {
+  if (act) {
     const float* src_blk = nullptr;
     if (wk.start == START_INIT && p.init) {
       int row = n;
@@ -662,21 +673,23 @@ void prefill_scan_kernel(PrefillParams p) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    scan_chunk<NB, NW>(srec0, srec0 + vt_off, 16 * NB * w, sout[0][w], min(CHUNK, len - j * CHUNK), wk.zero_v,
-                   wk.write_out, lane, S);
+    if (act)
+      scan_chunk<NB, NW>(srec0, srec0 + vt_off, 16 * NB * w, sout[0][w], min(CHUNK, len - j * CHUNK),
+                         wk.zero_v, wk.write_out, lane, S);
     if (j + 1 >= je) break;
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    scan_chunk<NB, NW>(srec1, srec1 + vt_off, 16 * NB * w, sout[1][w], min(CHUNK, len - (j + 1) * CHUNK),
-                   wk.zero_v, wk.write_out, lane, S);
+    if (act)
+      scan_chunk<NB, NW>(srec1, srec1 + vt_off, 16 * NB * w, sout[1][w], min(CHUNK, len - (j + 1) * CHUNK),
+                         wk.zero_v, wk.write_out, lane, S);
   }
   // Output tiles of the last chunk complete before the copy waves store them.
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 
-  if (wk.fin_blk) {
+  if (wk.fin_blk && act) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       float* dst = wk.fin_blk + v0 + 16 * nb + nl;
