@@ -8,8 +8,9 @@
 // Two forms of the same recurrence (the bounded-gate KDA step of vLLM PR #55737,
 // opening commit message and "Purpose"), chosen by the number of (row, head) pairs:
 //
-// Step form (many pairs, bandwidth-bound; also the fused output norm).  One
-// workgroup of 256 threads per (row b, head h, value tile of BV = 32 or 128 columns):
+// Step form (many pairs, bandwidth-bound; also the fused output norm).  A workgroup
+// of 256 threads takes one item (row b, head h, value tile of BV = 32 or 128 columns)
+// at a time, one workgroup per CU looping over the items:
 // the [128 x BV] fp32 state stays in registers for all T steps; thread (rg, cl) owns
 // rows rg*R .. rg*R+R-1 and value columns 4cl .. 4cl+3, so every store of a state row
 // segment is a contiguous BV*4-byte run and a wave writes whole 128-byte lines.
@@ -81,7 +82,34 @@ __global__ __launch_bounds__(256) void verify_step_kernel(VerifyParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int blk = blockIdx.x;
+  // Persistent: the grid holds one workgroup per CU and each takes items (row, head,
+  // value tile) gridDim.x apart.  The next item's pool state is loaded into registers
+  // when the current item's steps begin, so each workgroup's pool reads overlap its own
+  // state writes instead of all reads queueing at the start of the call.
+  const int nitems = p.B * p.H * NVT;
+  const int cl = tid % NCG;
+  const int rg = tid / NCG;
+  const int row0 = rg * R;
+  const int64_t head_elems = static_cast<int64_t>(D) * D;
+  auto state_src = [&](int it) -> const float* {   // this thread's rows, or null (padding)
+    const int tile = it % NVT, rest = it / NVT, hh = rest % p.H, bb = rest / p.H;
+    const int sl = p.idx[bb];
+    if (sl < 0 || sl >= p.slots) return nullptr;
+    return p.pool + (static_cast<int64_t>(sl) * p.H + hh) * head_elems +
+           static_cast<int64_t>(row0) * D + tile * BV + 4 * cl;
+  };
+  auto load_state = [&](int it, float4 (&dst)[R]) {
+    const float* src = it < nitems ? state_src(it) : nullptr;
+    if (src) {
+#pragma unroll
+      for (int j = 0; j < R; ++j) dst[j] = *reinterpret_cast<const float4*>(src + j * D);
+    }
+  };
+  float4 Sn[R];
+  load_state(blockIdx.x, Sn);
+  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+  __syncthreads();   // the previous item's LDS tables are no longer read
+  int blk = item;
   const int vt = blk % NVT;
   blk /= NVT;
   const int h = blk % p.H;
@@ -101,7 +129,8 @@ __global__ __launch_bounds__(256) void verify_step_kernel(VerifyParams p) {
         if (NORM && c == 0 && p.rstd) p.rstd[orow * p.H + h] = __builtin_amdgcn_rsqf(p.norm_eps);
       }
     }
-    return;
+    load_state(item + gridDim.x, Sn);
+    continue;
   }
 
   // ---------------- prologue: per-token norms, gates and beta into LDS.
@@ -152,19 +181,12 @@ __global__ __launch_bounds__(256) void verify_step_kernel(VerifyParams p) {
     s_orow[t] = p.out_idx ? p.out_idx[bt] : bt;
   }
 
-  // ---------------- gather the start state from the pool.
-  const int cl = tid % NCG;
-  const int rg = tid / NCG;
-  const int row0 = rg * R;
-  const int64_t head_elems = static_cast<int64_t>(D) * D;
+  // ---------------- the start state, gathered from the pool during the previous item.
   float4 S[R];
-  {
-    const float* src = p.pool + (static_cast<int64_t>(slot) * p.H + h) * head_elems +
-                       static_cast<int64_t>(row0) * D + v0 + 4 * cl;
 #pragma unroll
-    for (int j = 0; j < R; ++j) S[j] = *reinterpret_cast<const float4*>(src + j * D);
-  }
+  for (int j = 0; j < R; ++j) S[j] = Sn[j];
   __syncthreads();
+  load_state(item + gridDim.x, Sn);
 
   // ---------------- the T steps.
   for (int t = 0; t < T; ++t) {
@@ -258,6 +280,7 @@ __global__ __launch_bounds__(256) void verify_step_kernel(VerifyParams p) {
       }
     }
   }
+  }   // items
 }
 
 template <int BV, bool NORM>
@@ -281,7 +304,13 @@ hipError_t launch_verify_bv(const VerifyParams& p, hipStream_t s) {
                                static_cast<int>(verify_lds_bytes<BV, NORM>(KDA_MAX_STEPS_INTERNAL)));
   });
   if (e != hipSuccess) return e;
-  const dim3 grid(static_cast<unsigned>(p.B) * p.H * (D / BV));
+  int cus = 0;
+  if ((e = current_device_cus(&cus)) != hipSuccess) return e;
+  // One workgroup per CU (64 x 8 x 16 heads, 1024 items: warm 108.6 -> 106.6 us, after a
+  // prefill 124.5 -> 118.1 us, after a 1 GiB overwrite 143 -> 134 us, against one
+  // workgroup per item; 192, 320, 384 or 512 workgroups were slower).
+  const int64_t items = static_cast<int64_t>(p.B) * p.H * (D / BV);
+  const dim3 grid(static_cast<unsigned>(cus > 0 && items > cus ? cus : items));
   hipLaunchKernelGGL((verify_step_kernel<BV, NORM>), grid, dim3(256), lds, s, p);
   return hipGetLastError();
 }
