@@ -10,7 +10,7 @@
 //
 // Step form (many pairs, bandwidth-bound; also the fused output norm).  A workgroup
 // of 256 threads takes one item (row b, head h, value tile of BV = 32 or 128 columns)
-// at a time, one workgroup per CU looping over the items:
+// at a time (one workgroup per item, or with many 128-column items one per CU looping):
 // the [128 x BV] fp32 state stays in registers for all T steps; thread (rg, cl) owns
 // rows rg*R .. rg*R+R-1 and value columns 4cl .. 4cl+3, so every store of a state row
 // segment is a contiguous BV*4-byte run and a wave writes whole 128-byte lines.
@@ -82,10 +82,11 @@ __global__ __launch_bounds__(256) void verify_step_kernel(VerifyParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // Persistent: the grid holds one workgroup per CU and each takes items (row, head,
-  // value tile) gridDim.x apart.  The next item's pool state is loaded into registers
-  // when the current item's steps begin, so each workgroup's pool reads overlap its own
-  // state writes instead of all reads queueing at the start of the call.
+  // With more items (row, head, value tile) than workgroups, each workgroup takes items
+  // gridDim.x apart and loads the next item's pool state into registers when the
+  // current item's steps begin, so its pool reads overlap its own state writes instead
+  // of all reads queueing at the start of the call.  With one item per workgroup the
+  // state is gathered after the prologue.
   const int nitems = p.B * p.H * NVT;
   const int cl = tid % NCG;
   const int rg = tid / NCG;
@@ -105,8 +106,9 @@ __global__ __launch_bounds__(256) void verify_step_kernel(VerifyParams p) {
       for (int j = 0; j < R; ++j) dst[j] = *reinterpret_cast<const float4*>(src + j * D);
     }
   };
+  const bool looping = static_cast<int>(gridDim.x) < nitems;
   float4 Sn[R];
-  load_state(blockIdx.x, Sn);
+  if (looping) load_state(blockIdx.x, Sn);
   for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
   __syncthreads();   // the previous item's LDS tables are no longer read
   int blk = item;
@@ -129,7 +131,7 @@ __global__ __launch_bounds__(256) void verify_step_kernel(VerifyParams p) {
         if (NORM && c == 0 && p.rstd) p.rstd[orow * p.H + h] = __builtin_amdgcn_rsqf(p.norm_eps);
       }
     }
-    load_state(item + gridDim.x, Sn);
+    if (looping) load_state(item + gridDim.x, Sn);
     continue;
   }
 
@@ -181,12 +183,13 @@ __global__ __launch_bounds__(256) void verify_step_kernel(VerifyParams p) {
     s_orow[t] = p.out_idx ? p.out_idx[bt] : bt;
   }
 
-  // ---------------- the start state, gathered from the pool during the previous item.
+  // ---------------- the start state (gathered during the previous item when looping).
+  if (!looping) load_state(item, Sn);
   float4 S[R];
 #pragma unroll
   for (int j = 0; j < R; ++j) S[j] = Sn[j];
   __syncthreads();
-  load_state(item + gridDim.x, Sn);
+  if (looping) load_state(item + gridDim.x, Sn);
 
   // ---------------- the T steps.
   for (int t = 0; t < T; ++t) {
@@ -306,11 +309,17 @@ hipError_t launch_verify_bv(const VerifyParams& p, hipStream_t s) {
   if (e != hipSuccess) return e;
   int cus = 0;
   if ((e = current_device_cus(&cus)) != hipSuccess) return e;
-  // One workgroup per CU (64 x 8 x 16 heads, 1024 items: warm 108.6 -> 106.6 us, after a
-  // prefill 124.5 -> 118.1 us, after a 1 GiB overwrite 143 -> 134 us, against one
-  // workgroup per item; 192, 320, 384 or 512 workgroups were slower).
+  // 128-column tiles with at least two items per CU: one looping workgroup per CU (64 x 8
+  // x 16 heads, 1024 items: warm 108.6 -> 106.6 us, after a prefill 124.5 -> 118.1 us,
+  // after a 1 GiB overwrite 143 -> 134 us, against one workgroup per item; 192, 320, 384
+  // or 512 workgroups were slower; 512 and 768 items: 59.9 -> 59.2, 84.3 -> 82.6 us).
+  // Otherwise one workgroup per item: with fewer items, or with 32-column tiles, whose
+  // items are short and latency-bound, looping workgroups were slower (256, 384 items:
+  // 33.7 -> 34.8, 45.6 -> 48.5 us; 32-column tiles at 448-960 items: 16.7 -> 24.6,
+  // 31.3 -> 45.7 us).
   const int64_t items = static_cast<int64_t>(p.B) * p.H * (D / BV);
-  const dim3 grid(static_cast<unsigned>(cus > 0 && items > cus ? cus : items));
+  const bool loop = BV == D && cus > 0 && items >= 2 * static_cast<int64_t>(cus);
+  const dim3 grid(static_cast<unsigned>(loop ? cus : items));
   hipLaunchKernelGGL((verify_step_kernel<BV, NORM>), grid, dim3(256), lds, s, p);
   return hipGetLastError();
 }
