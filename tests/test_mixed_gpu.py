@@ -198,6 +198,26 @@ def test_verify_then_commit_equals_prefill_of_accepted_prefix():
         assert np.array_equal(got[s], data["state_pool"].numpy()[s])
 
 
+def test_commit_looping_workgroups_with_skipped_rows():
+    """48 rows x 16 heads is more than two (row, head) items per CU on 256 CUs: each
+    workgroup loops, loading its next item before storing the current one.  Rows that
+    commit nothing (padding slots, no accepted token, more than T) sit among them and
+    leave their pool slots as they were."""
+    rng = np.random.default_rng(3112)
+    B, T, H, slots = 48, 4, 16, 64
+    inter = torch.from_numpy(rng.standard_normal((B, T, H, 128, 128), dtype=np.float32))
+    pool = torch.from_numpy(rng.standard_normal((slots, H, 128, 128), dtype=np.float32))
+    idx = rng.permutation(slots)[:B].astype(np.int32)
+    idx[0], idx[17], idx[B - 1] = -1, slots, -3
+    nacc = rng.integers(1, T + 1, size=B).astype(np.int32)
+    nacc[5], nacc[30] = 0, T + 1
+    want = O.commit_accepted(pool.numpy(), inter.numpy(), idx, nacc)
+    got = commit_accepted(inter.cuda(), torch.from_numpy(idx).cuda(),
+                          torch.from_numpy(nacc).cuda(), pool.cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), want)
+
+
 def test_commit_full_size_64x8_h16():
     """Full verify size: 64 rows, 8 steps, 16 heads, 256-slot pool, seeded intermediate."""
     rng = np.random.default_rng(3110)
