@@ -110,180 +110,180 @@ __global__ __launch_bounds__(256) void verify_step_kernel(VerifyParams p) {
   float4 Sn[R];
   if (looping) load_state(blockIdx.x, Sn);
   for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
-  __syncthreads();   // the previous item's LDS tables are no longer read
-  int blk = item;
-  const int vt = blk % NVT;
-  blk /= NVT;
-  const int h = blk % p.H;
-  const int b = blk / p.H;
-  const int v0 = vt * BV;
+    __syncthreads();   // the previous item's LDS tables are no longer read
+    int blk = item;
+    const int vt = blk % NVT;
+    blk /= NVT;
+    const int h = blk % p.H;
+    const int b = blk / p.H;
+    const int v0 = vt * BV;
 
-  const int slot = p.idx[b];
-  if (slot < 0 || slot >= p.slots) {
-    // Padding row: zero outputs (normalised or not), no state rows written; the norm's
-    // rstd of a zero row is 1/sqrt(eps).
-    for (int e = tid; e < T * BV; e += 256) {
-      const int t = e / BV, c = e % BV;
-      int64_t orow = static_cast<int64_t>(b) * T + t;
-      if (p.out_idx) orow = p.out_idx[orow];
-      if (orow >= 0 && orow < p.out_rows) {
-        p.out[orow * p.o_st + h * D + v0 + c] = 0;
-        if (NORM && c == 0 && p.rstd) p.rstd[orow * p.H + h] = __builtin_amdgcn_rsqf(p.norm_eps);
+    const int slot = p.idx[b];
+    if (slot < 0 || slot >= p.slots) {
+      // Padding row: zero outputs (normalised or not), no state rows written; the norm's
+      // rstd of a zero row is 1/sqrt(eps).
+      for (int e = tid; e < T * BV; e += 256) {
+        const int t = e / BV, c = e % BV;
+        int64_t orow = static_cast<int64_t>(b) * T + t;
+        if (p.out_idx) orow = p.out_idx[orow];
+        if (orow >= 0 && orow < p.out_rows) {
+          p.out[orow * p.o_st + h * D + v0 + c] = 0;
+          if (NORM && c == 0 && p.rstd) p.rstd[orow * p.H + h] = __builtin_amdgcn_rsqf(p.norm_eps);
+        }
+      }
+      if (looping) load_state(item + gridDim.x, Sn);
+      continue;
+    }
+
+    // ---------------- prologue: per-token norms, gates and beta into LDS.
+    const float eA = __builtin_amdgcn_exp2f(p.A_log[h] * LOG2E);
+    const float2 dtb = *reinterpret_cast<const float2*>(p.dt_bias + h * D + 2 * lane);
+    for (int t = wave; t < T; t += 4) {
+      const int64_t tok = static_cast<int64_t>(b) * T + t;
+      const uint32_t qw = *reinterpret_cast<const uint32_t*>(p.q + tok * p.q_st + h * D + 2 * lane);
+      const uint32_t kw = *reinterpret_cast<const uint32_t*>(p.k + tok * p.k_st + h * D + 2 * lane);
+      const uint32_t gw = *reinterpret_cast<const uint32_t*>(p.g + tok * p.g_st + h * D + 2 * lane);
+      const float q0 = bf16lo_to_f32(qw), q1 = bf16hi_to_f32(qw);
+      const float k0 = bf16lo_to_f32(kw), k1 = bf16hi_to_f32(kw);
+      const float g0 = bf16lo_to_f32(gw), g1 = bf16hi_to_f32(gw);
+      const float ssq = wave_sum(q0 * q0 + q1 * q1);
+      const float ssk = wave_sum(k0 * k0 + k1 * k1);
+      const float sqk = wave_sum(q0 * k0 + q1 * k1);
+      const float rq = __builtin_amdgcn_rsqf(ssq + L2_EPS);
+      const float rk = __builtin_amdgcn_rsqf(ssk + L2_EPS);
+      const float a0 = __builtin_amdgcn_exp2f(p.lb_log2e * sigmoid_f32(eA * (g0 + dtb.x)));
+      const float a1 = __builtin_amdgcn_exp2f(p.lb_log2e * sigmoid_f32(eA * (g1 + dtb.y)));
+      *reinterpret_cast<float2*>(s_alpha + t * D + 2 * lane) = make_float2(a0, a1);
+      *reinterpret_cast<float2*>(s_khat + t * D + 2 * lane) = make_float2(k0 * rk, k1 * rk);
+      *reinterpret_cast<float2*>(s_qhat + t * D + 2 * lane) = make_float2(q0 * rq, q1 * rq);
+      if (2 * lane < BV) {
+        const uint32_t vw =
+            *reinterpret_cast<const uint32_t*>(p.v + tok * p.v_st + h * D + v0 + 2 * lane);
+        s_v[t * BV + 2 * lane] = bf16lo_to_f32(vw);
+        s_v[t * BV + 2 * lane + 1] = bf16hi_to_f32(vw);
+      }
+      if (lane == 0) {
+        s_beta[t] = sigmoid_f32(bf16_to_f32(p.beta[tok * p.b_st + h]));
+        s_kq[t] = sqk * rq * rk;
+      }
+      if (NORM) {
+        // the output gate of this token's output row (rows outside the output are never
+        // stored; their gate is not read)
+        const int64_t orow = p.out_idx ? static_cast<int64_t>(p.out_idx[tok]) : tok;
+        uint32_t gw2 = 0;
+        if (orow >= 0 && orow < p.out_rows)
+          gw2 = *reinterpret_cast<const uint32_t*>(p.out_gate + orow * p.og_st + h * D + 2 * lane);
+        *reinterpret_cast<uint32_t*>(s_gate + t * D + 2 * lane) = gw2;
       }
     }
-    if (looping) load_state(item + gridDim.x, Sn);
-    continue;
-  }
 
-  // ---------------- prologue: per-token norms, gates and beta into LDS.
-  const float eA = __builtin_amdgcn_exp2f(p.A_log[h] * LOG2E);
-  const float2 dtb = *reinterpret_cast<const float2*>(p.dt_bias + h * D + 2 * lane);
-  for (int t = wave; t < T; t += 4) {
-    const int64_t tok = static_cast<int64_t>(b) * T + t;
-    const uint32_t qw = *reinterpret_cast<const uint32_t*>(p.q + tok * p.q_st + h * D + 2 * lane);
-    const uint32_t kw = *reinterpret_cast<const uint32_t*>(p.k + tok * p.k_st + h * D + 2 * lane);
-    const uint32_t gw = *reinterpret_cast<const uint32_t*>(p.g + tok * p.g_st + h * D + 2 * lane);
-    const float q0 = bf16lo_to_f32(qw), q1 = bf16hi_to_f32(qw);
-    const float k0 = bf16lo_to_f32(kw), k1 = bf16hi_to_f32(kw);
-    const float g0 = bf16lo_to_f32(gw), g1 = bf16hi_to_f32(gw);
-    const float ssq = wave_sum(q0 * q0 + q1 * q1);
-    const float ssk = wave_sum(k0 * k0 + k1 * k1);
-    const float sqk = wave_sum(q0 * k0 + q1 * k1);
-    const float rq = __builtin_amdgcn_rsqf(ssq + L2_EPS);
-    const float rk = __builtin_amdgcn_rsqf(ssk + L2_EPS);
-    const float a0 = __builtin_amdgcn_exp2f(p.lb_log2e * sigmoid_f32(eA * (g0 + dtb.x)));
-    const float a1 = __builtin_amdgcn_exp2f(p.lb_log2e * sigmoid_f32(eA * (g1 + dtb.y)));
-    *reinterpret_cast<float2*>(s_alpha + t * D + 2 * lane) = make_float2(a0, a1);
-    *reinterpret_cast<float2*>(s_khat + t * D + 2 * lane) = make_float2(k0 * rk, k1 * rk);
-    *reinterpret_cast<float2*>(s_qhat + t * D + 2 * lane) = make_float2(q0 * rq, q1 * rq);
-    if (2 * lane < BV) {
-      const uint32_t vw =
-          *reinterpret_cast<const uint32_t*>(p.v + tok * p.v_st + h * D + v0 + 2 * lane);
-      s_v[t * BV + 2 * lane] = bf16lo_to_f32(vw);
-      s_v[t * BV + 2 * lane + 1] = bf16hi_to_f32(vw);
+    // Output row of each step (the scatter index, when given).
+    for (int t = tid; t < T; t += 256) {
+      const int bt = b * T + t;
+      s_orow[t] = p.out_idx ? p.out_idx[bt] : bt;
     }
-    if (lane == 0) {
-      s_beta[t] = sigmoid_f32(bf16_to_f32(p.beta[tok * p.b_st + h]));
-      s_kq[t] = sqk * rq * rk;
+
+    // ---------------- the start state (gathered during the previous item when looping).
+    if (!looping) load_state(item, Sn);
+    float4 S[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) S[j] = Sn[j];
+    __syncthreads();
+    if (looping) load_state(item + gridDim.x, Sn);
+
+    // ---------------- the T steps.
+    for (int t = 0; t < T; ++t) {
+      const float* al = s_alpha + t * D + row0;
+      const float* kh = s_khat + t * D + row0;
+      const float* qh = s_qhat + t * D + row0;
+      float4 r = make_float4(0.f, 0.f, 0.f, 0.f), y = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        const float a = al[j], kk = kh[j], qq = qh[j];
+        S[j].x *= a; S[j].y *= a; S[j].z *= a; S[j].w *= a;
+        r.x += S[j].x * kk; r.y += S[j].y * kk; r.z += S[j].z * kk; r.w += S[j].w * kk;
+        y.x += S[j].x * qq; y.y += S[j].y * qq; y.z += S[j].z * qq; y.w += S[j].w * qq;
+      }
+#pragma unroll
+      for (int off = NCG; off < 64; off <<= 1) {
+        r.x += __shfl_xor(r.x, off); r.y += __shfl_xor(r.y, off);
+        r.z += __shfl_xor(r.z, off); r.w += __shfl_xor(r.w, off);
+        y.x += __shfl_xor(y.x, off); y.y += __shfl_xor(y.y, off);
+        y.z += __shfl_xor(y.z, off); y.w += __shfl_xor(y.w, off);
+      }
+      float* part = s_part + (t & 1) * (4 * 2 * BV);
+      if (lane < NCG) {
+        *reinterpret_cast<float4*>(part + (wave * 2 + 0) * BV + 4 * cl) = r;
+        *reinterpret_cast<float4*>(part + (wave * 2 + 1) * BV + 4 * cl) = y;
+      }
+      __syncthreads();
+      float4 rr = make_float4(0.f, 0.f, 0.f, 0.f), yy = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float4 a = *reinterpret_cast<const float4*>(part + (w * 2 + 0) * BV + 4 * cl);
+        const float4 c = *reinterpret_cast<const float4*>(part + (w * 2 + 1) * BV + 4 * cl);
+        rr.x += a.x; rr.y += a.y; rr.z += a.z; rr.w += a.w;
+        yy.x += c.x; yy.y += c.y; yy.z += c.z; yy.w += c.w;
+      }
+      const float4 vv = *reinterpret_cast<const float4*>(s_v + t * BV + 4 * cl);
+      const float be = s_beta[t], kq = s_kq[t];
+      float4 u;
+      u.x = be * (vv.x - rr.x); u.y = be * (vv.y - rr.y);
+      u.z = be * (vv.z - rr.z); u.w = be * (vv.w - rr.w);
+
+      float* dst = p.inter +
+                   ((static_cast<int64_t>(b) * T + t) * p.H + h) * head_elems +
+                   static_cast<int64_t>(row0) * D + v0 + 4 * cl;
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        const float kk = kh[j];
+        S[j].x += kk * u.x; S[j].y += kk * u.y; S[j].z += kk * u.z; S[j].w += kk * u.w;
+        const f32x4 sv = {S[j].x, S[j].y, S[j].z, S[j].w};
+        __builtin_nontemporal_store(sv, reinterpret_cast<f32x4*>(dst + j * D));
+      }
+      if (rg == 0) {
+        const float s = p.scale;
+        const float4 o = make_float4(s * (yy.x + kq * u.x), s * (yy.y + kq * u.y),
+                                     s * (yy.z + kq * u.z), s * (yy.w + kq * u.w));
+        if (NORM) {
+          // Row t of the decay table is dead once this step's barrier has passed (every
+          // thread read its entries before it): the fp32 output row waits there for the norm.
+          *reinterpret_cast<float4*>(s_alpha + t * D + 4 * cl) = o;
+        } else {
+          const int64_t orow = s_orow[t];
+          if (orow >= 0 && orow < p.out_rows)
+            *reinterpret_cast<uint2*>(p.out + orow * p.o_st + h * D + v0 + 4 * cl) =
+                make_uint2(pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w));
+        }
+      }
     }
     if (NORM) {
-      // the output gate of this token's output row (rows outside the output are never
-      // stored; their gate is not read)
-      const int64_t orow = p.out_idx ? static_cast<int64_t>(p.out_idx[tok]) : tok;
-      uint32_t gw2 = 0;
-      if (orow >= 0 && orow < p.out_rows)
-        gw2 = *reinterpret_cast<const uint32_t*>(p.out_gate + orow * p.og_st + h * D + 2 * lane);
-      *reinterpret_cast<uint32_t*>(s_gate + t * D + 2 * lane) = gw2;
-    }
-  }
-
-  // Output row of each step (the scatter index, when given).
-  for (int t = tid; t < T; t += 256) {
-    const int bt = b * T + t;
-    s_orow[t] = p.out_idx ? p.out_idx[bt] : bt;
-  }
-
-  // ---------------- the start state (gathered during the previous item when looping).
-  if (!looping) load_state(item, Sn);
-  float4 S[R];
+      // The norm of every output row after the last step, off the steps' critical path:
+      // groups of 32 threads take one row each (4 channels per thread), reduce its squares
+      // across the group and store y = o * rstd * weight * sigmoid(gate).
+      __syncthreads();
+      const int grp = tid >> 5, c4 = 4 * (tid & 31);
+      const float4 w4 = *reinterpret_cast<const float4*>(p.norm_w + c4);
+      for (int t = grp; t < T; t += 8) {
+        const float4 o = *reinterpret_cast<const float4*>(s_alpha + t * D + c4);
+        float ss = o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
 #pragma unroll
-  for (int j = 0; j < R; ++j) S[j] = Sn[j];
-  __syncthreads();
-  if (looping) load_state(item + gridDim.x, Sn);
-
-  // ---------------- the T steps.
-  for (int t = 0; t < T; ++t) {
-    const float* al = s_alpha + t * D + row0;
-    const float* kh = s_khat + t * D + row0;
-    const float* qh = s_qhat + t * D + row0;
-    float4 r = make_float4(0.f, 0.f, 0.f, 0.f), y = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-      const float a = al[j], kk = kh[j], qq = qh[j];
-      S[j].x *= a; S[j].y *= a; S[j].z *= a; S[j].w *= a;
-      r.x += S[j].x * kk; r.y += S[j].y * kk; r.z += S[j].z * kk; r.w += S[j].w * kk;
-      y.x += S[j].x * qq; y.y += S[j].y * qq; y.z += S[j].z * qq; y.w += S[j].w * qq;
-    }
-#pragma unroll
-    for (int off = NCG; off < 64; off <<= 1) {
-      r.x += __shfl_xor(r.x, off); r.y += __shfl_xor(r.y, off);
-      r.z += __shfl_xor(r.z, off); r.w += __shfl_xor(r.w, off);
-      y.x += __shfl_xor(y.x, off); y.y += __shfl_xor(y.y, off);
-      y.z += __shfl_xor(y.z, off); y.w += __shfl_xor(y.w, off);
-    }
-    float* part = s_part + (t & 1) * (4 * 2 * BV);
-    if (lane < NCG) {
-      *reinterpret_cast<float4*>(part + (wave * 2 + 0) * BV + 4 * cl) = r;
-      *reinterpret_cast<float4*>(part + (wave * 2 + 1) * BV + 4 * cl) = y;
-    }
-    __syncthreads();
-    float4 rr = make_float4(0.f, 0.f, 0.f, 0.f), yy = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float4 a = *reinterpret_cast<const float4*>(part + (w * 2 + 0) * BV + 4 * cl);
-      const float4 c = *reinterpret_cast<const float4*>(part + (w * 2 + 1) * BV + 4 * cl);
-      rr.x += a.x; rr.y += a.y; rr.z += a.z; rr.w += a.w;
-      yy.x += c.x; yy.y += c.y; yy.z += c.z; yy.w += c.w;
-    }
-    const float4 vv = *reinterpret_cast<const float4*>(s_v + t * BV + 4 * cl);
-    const float be = s_beta[t], kq = s_kq[t];
-    float4 u;
-    u.x = be * (vv.x - rr.x); u.y = be * (vv.y - rr.y);
-    u.z = be * (vv.z - rr.z); u.w = be * (vv.w - rr.w);
-
-    float* dst = p.inter +
-                 ((static_cast<int64_t>(b) * T + t) * p.H + h) * head_elems +
-                 static_cast<int64_t>(row0) * D + v0 + 4 * cl;
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-      const float kk = kh[j];
-      S[j].x += kk * u.x; S[j].y += kk * u.y; S[j].z += kk * u.z; S[j].w += kk * u.w;
-      const f32x4 sv = {S[j].x, S[j].y, S[j].z, S[j].w};
-      __builtin_nontemporal_store(sv, reinterpret_cast<f32x4*>(dst + j * D));
-    }
-    if (rg == 0) {
-      const float s = p.scale;
-      const float4 o = make_float4(s * (yy.x + kq * u.x), s * (yy.y + kq * u.y),
-                                   s * (yy.z + kq * u.z), s * (yy.w + kq * u.w));
-      if (NORM) {
-        // Row t of the decay table is dead once this step's barrier has passed (every
-        // thread read its entries before it): the fp32 output row waits there for the norm.
-        *reinterpret_cast<float4*>(s_alpha + t * D + 4 * cl) = o;
-      } else {
+        for (int off = 1; off < 32; off <<= 1) ss += __shfl_xor(ss, off);
+        const float rs = __builtin_amdgcn_rsqf(ss * (1.0f / D) + p.norm_eps);
+        const uint2 gr = *reinterpret_cast<const uint2*>(s_gate + t * D + c4);
+        const float y0 = o.x * rs * w4.x * sigmoid_f32(bf16lo_to_f32(gr.x));
+        const float y1 = o.y * rs * w4.y * sigmoid_f32(bf16hi_to_f32(gr.x));
+        const float y2 = o.z * rs * w4.z * sigmoid_f32(bf16lo_to_f32(gr.y));
+        const float y3 = o.w * rs * w4.w * sigmoid_f32(bf16hi_to_f32(gr.y));
         const int64_t orow = s_orow[t];
-        if (orow >= 0 && orow < p.out_rows)
-          *reinterpret_cast<uint2*>(p.out + orow * p.o_st + h * D + v0 + 4 * cl) =
-              make_uint2(pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w));
+        if (orow >= 0 && orow < p.out_rows) {
+          *reinterpret_cast<uint2*>(p.out + orow * p.o_st + h * D + c4) =
+              make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
+          if ((tid & 31) == 0 && p.rstd) p.rstd[orow * p.H + h] = rs;
+        }
       }
     }
   }
-  if (NORM) {
-    // The norm of every output row after the last step, off the steps' critical path:
-    // groups of 32 threads take one row each (4 channels per thread), reduce its squares
-    // across the group and store y = o * rstd * weight * sigmoid(gate).
-    __syncthreads();
-    const int grp = tid >> 5, c4 = 4 * (tid & 31);
-    const float4 w4 = *reinterpret_cast<const float4*>(p.norm_w + c4);
-    for (int t = grp; t < T; t += 8) {
-      const float4 o = *reinterpret_cast<const float4*>(s_alpha + t * D + c4);
-      float ss = o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
-#pragma unroll
-      for (int off = 1; off < 32; off <<= 1) ss += __shfl_xor(ss, off);
-      const float rs = __builtin_amdgcn_rsqf(ss * (1.0f / D) + p.norm_eps);
-      const uint2 gr = *reinterpret_cast<const uint2*>(s_gate + t * D + c4);
-      const float y0 = o.x * rs * w4.x * sigmoid_f32(bf16lo_to_f32(gr.x));
-      const float y1 = o.y * rs * w4.y * sigmoid_f32(bf16hi_to_f32(gr.x));
-      const float y2 = o.z * rs * w4.z * sigmoid_f32(bf16lo_to_f32(gr.y));
-      const float y3 = o.w * rs * w4.w * sigmoid_f32(bf16hi_to_f32(gr.y));
-      const int64_t orow = s_orow[t];
-      if (orow >= 0 && orow < p.out_rows) {
-        *reinterpret_cast<uint2*>(p.out + orow * p.o_st + h * D + c4) =
-            make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
-        if ((tid & 31) == 0 && p.rstd) p.rstd[orow * p.H + h] = rs;
-      }
-    }
-  }
-  }   // items
 }
 
 template <int BV, bool NORM>
