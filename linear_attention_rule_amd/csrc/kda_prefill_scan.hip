@@ -802,12 +802,14 @@ int prefill_segments(int N, int T_total, int H, int cus) {
   // Segments pay off when the pairs leave most CUs idle and sequences are long: the
   // critical path goes from G segment lengths to about two, for about three times the
   // scan work spread over otherwise idle CUs.  G is the largest count whose phase A
-  // (2 workgroups for segment 0, 4 per middle segment: 4-wave scans of 64 columns)
-  // fits the CUs at once, with at least SEG_MIN_CHUNKS chunks per segment on average.
+  // (4 workgroups per segment of G - 1: segment 0 on half-active four-wave scans, the
+  // middle segments' maps and offsets on full ones) and phase C (4 two-wave workgroups
+  // per segment of G - 1) fit the CUs at once, with at least SEG_MIN_CHUNKS chunks per
+  // segment on average.
   const int64_t pairs = static_cast<int64_t>(N) * H;
   if (N <= 0 || pairs > SEG_MAX_PAIRS || pairs * 8 > cus) return 1;
   const int64_t avg_chunks = static_cast<int64_t>(T_total) / CHUNK / N;
-  int64_t G = (cus / pairs - 2) / 4 + 2;
+  int64_t G = cus / pairs / 4 + 1;
   G = std::min<int64_t>(G, SEG_MAX);
   G = std::min<int64_t>(G, avg_chunks / SEG_MIN_CHUNKS);
   return G >= 3 ? static_cast<int>(G) : 1;

@@ -411,6 +411,7 @@ def test_prefill_full_size_every_pair(case):
     ([64 * 40 + 17], 2, "per_seq"),
     ([3000, 100, 1500], 2, "pool"),
     ([64 * 33, 64 * 12], 1, None),
+    ([64 * 24 + 5], 14, "per_seq"),   # 14 pairs: G = 5, phases A and C on 224 workgroups
 ])
 def test_prefill_segmented_scan(lens, H, init):
     case = W.PrefillCase(f"seg_{len(lens)}x{H}", lens, H, init=init, pool_slots=5,
