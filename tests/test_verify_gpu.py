@@ -172,26 +172,27 @@ def test_verify_padding_rows_untouched():
         assert torch.all(inter[b] == sentinel)
 
 
-@pytest.mark.parametrize("B", [33, 40])
-def test_verify_looping_workgroups_with_padding_rows(B):
-    """B x 16 heads at 128-column tiles is more than two items per CU on 256 CUs (528 and
-    640 items): each workgroup loops over items and prefetches the next item's state.
-    Padding rows (slot -1 and slot == num_slots) sit among them; their outputs are zero and
-    their state rows untouched, and every live row matches the oracle."""
-    case = W.VerifyCase(f"v_loop{B}", B, 8, 16, pool_slots=64, seed=2110 + B,
+@pytest.mark.parametrize("B,T", [(33, 8), (40, 8), (32, 19)])
+def test_verify_looping_workgroups_with_padding_rows(B, T):
+    """B x 16 heads at 128-column tiles is at least two items per CU on 256 CUs (528, 640
+    and 512 items): each workgroup loops over items and prefetches the next item's state
+    (T = 19: a longer step loop per item).  Padding rows (slot -1 and slot ==
+    num_slots) sit among them; their outputs are zero and their state rows untouched, and
+    every live row matches the oracle."""
+    case = W.VerifyCase(f"v_loop{B}x{T}", B, T, 16, pool_slots=64, seed=2110 + B + T,
                         padding_rows=[0, 7, B - 1])
     data = W.make_verify(case)
     data["state_idx"][12] = 64        # == num_slots: out of range, treated as padding
     print(f"case {case.name} seed {case.seed}", flush=True)
     d = _dev(data)
     sentinel = -2.5
-    inter = torch.full((B, 8, 16, 128, 128), sentinel, dtype=torch.float32, device="cuda")
-    out = torch.full((B * 8, 16, 128), 3.0, dtype=torch.bfloat16, device="cuda")
+    inter = torch.full((B, T, 16, 128, 128), sentinel, dtype=torch.float32, device="cuda")
+    out = torch.full((B * T, 16, 128), 3.0, dtype=torch.bfloat16, device="cuda")
     _call(d, intermediate=inter, out=out)
     torch.cuda.synchronize()
     _check(data, out, inter)
     for b in (0, 7, 12, B - 1):
-        assert torch.all(out[b * 8:(b + 1) * 8] == 0)
+        assert torch.all(out[b * T:(b + 1) * T] == 0)
         assert torch.all(inter[b] == sentinel)
 
 
