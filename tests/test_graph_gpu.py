@@ -79,11 +79,13 @@ def test_prefill_graph_replays_match_eager(lens, H):
     _replay_and_compare(graph, [out, fin], [ref_out, ref_fin])
 
 
-def test_verify_graph_replays_match_eager():
-    case = W.VerifyCase("graph_v", 10, 8, 3, pool_slots=16, seed=4400, padding_rows=[3])
+@pytest.mark.parametrize("B,H", [(10, 3), (36, 16)])   # block form; looping step form
+def test_verify_graph_replays_match_eager(B, H):
+    T = 8
+    case = W.VerifyCase(f"graph_v{B}x{H}", B, T, H, pool_slots=64, seed=4400 + B,
+                        padding_rows=[3])
     data = W.make_verify(case)
     d = _dev(data)
-    B, T, H = 10, 8, 3
     out = torch.empty((B * T, H, 128), dtype=torch.bfloat16, device="cuda")
     inter = torch.empty((B, T, H, 128, 128), dtype=torch.float32, device="cuda")
 
