@@ -586,13 +586,17 @@ void prefill_scan_kernel(PrefillParams p) {
     // One wave touches each 128-byte line of value rows: the two 64-byte halves of a
     // line belong to value slices 2k and 2k+1, and a workgroup's copy waves share it.
     const bool touch_v = copy_vt && cw == 0 && (wk.vs & 1) == 0;
-    const bool store = has_vt && wk.write_out && ((wk.active >> w) & 1);
+    // Only phase A has inactive compute waves and scans without outputs; elsewhere these
+    // conditions fold away at compile time.
+    constexpr bool SEG_A = MODE == MODE_SEG_A;
+    const bool store = has_vt && (!SEG_A || (wk.write_out && ((wk.active >> w) & 1)));
+    const bool full_rec = !SEG_A || wk.write_out;
     const uint32_t lds0 = lds_addr(srec0), lds1 = lds_addr(srec1);
     const uint32_t sink = lds_addr(touch_sink[cw]);
     for (int j = jb; j < je; ++j) {
       const int par = (j - jb) & 1;
       if (j == jb) {
-        CC(p, recbase, cs, ce, jb, h, wk.vs * BV, cw, copy_vt, lane, lds0, vt_off).all(wk.write_out);
+        CC(p, recbase, cs, ce, jb, h, wk.vs * BV, cw, copy_vt, lane, lds0, vt_off).all(full_rec);
         if (TOUCH) {
           CC(p, recbase, cs, ce, min(jb + 1, je - 1), h, wk.vs * BV, cw, copy_vt, lane, lds1, vt_off)
               .touch(lane, sink, cw, wk.share, wk.nshare, touch_v);
@@ -608,7 +612,8 @@ void prefill_scan_kernel(PrefillParams p) {
       if (wk.write_out && p.out_idx && cw == 0)
         copy_out_index(p, cs, ce, j, lane, lds_addr(sidx[par]));
       if (j + 1 < je) {
-        CC(p, recbase, cs, ce, j + 1, h, wk.vs * BV, cw, copy_vt, lane, par ? lds0 : lds1, vt_off).all(wk.write_out);
+        CC(p, recbase, cs, ce, j + 1, h, wk.vs * BV, cw, copy_vt, lane, par ? lds0 : lds1, vt_off)
+            .all(full_rec);
         if (TOUCH) {
           CC(p, recbase, cs, ce, min(j + 2, je - 1), h, wk.vs * BV, cw, copy_vt, lane, lds0, vt_off)
               .touch(lane, sink, cw, wk.share, wk.nshare, touch_v);
@@ -634,7 +639,7 @@ void prefill_scan_kernel(PrefillParams p) {
 
   // Start state: S[nb][cb][r] = S[16cb + 4g + r][v0 + 16nb + nl].  An inactive compute
   // wave keeps the workgroup's barrier count and does nothing else.
-  const bool act = (wk.active >> w) & 1;
+  const bool act = MODE != MODE_SEG_A || ((wk.active >> w) & 1);
   f32x4 S[NB][8];
   if (act) {
     const float* src_blk = nullptr;
