@@ -56,7 +56,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 // leaves its fp32 output row in LDS (in the step's dead decay-table row), and after the
 // last step groups of 32 threads normalise the rows and store y = o * rstd * weight *
 // sigmoid(gate), with the gate rows staged in the prologue.
-template <int BV, bool NORM>
+template <int BV, bool NORM, bool LOOP>
 __global__ __launch_bounds__(256) void verify_step_kernel(VerifyParams p) {
   constexpr int NCG = BV / 4;      // column groups (float4) per state row
   constexpr int NRG = 256 / NCG;   // row groups
@@ -82,11 +82,11 @@ __global__ __launch_bounds__(256) void verify_step_kernel(VerifyParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // With more items (row, head, value tile) than workgroups, each workgroup takes items
+  // LOOP: fewer workgroups than items (row, head, value tile); each workgroup takes items
   // gridDim.x apart and loads the next item's pool state into registers when the
   // current item's steps begin, so its pool reads overlap its own state writes instead
-  // of all reads queueing at the start of the call.  With one item per workgroup the
-  // state is gathered after the prologue.
+  // of all reads queueing at the start of the call.  Otherwise one item per workgroup,
+  // its state gathered after the prologue.
   const int nitems = p.B * p.H * NVT;
   const int cl = tid % NCG;
   const int rg = tid / NCG;
@@ -106,11 +106,8 @@ __global__ __launch_bounds__(256) void verify_step_kernel(VerifyParams p) {
       for (int j = 0; j < R; ++j) dst[j] = *reinterpret_cast<const float4*>(src + j * D);
     }
   };
-  const bool looping = static_cast<int>(gridDim.x) < nitems;
   float4 Sn[R];
-  if (looping) load_state(blockIdx.x, Sn);
-  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
-    __syncthreads();   // the previous item's LDS tables are no longer read
+  auto run_item = [&](const int item) {
     int blk = item;
     const int vt = blk % NVT;
     blk /= NVT;
@@ -131,8 +128,8 @@ __global__ __launch_bounds__(256) void verify_step_kernel(VerifyParams p) {
           if (NORM && c == 0 && p.rstd) p.rstd[orow * p.H + h] = __builtin_amdgcn_rsqf(p.norm_eps);
         }
       }
-      if (looping) load_state(item + gridDim.x, Sn);
-      continue;
+      if (LOOP) load_state(item + gridDim.x, Sn);
+      return;
     }
 
     // ---------------- prologue: per-token norms, gates and beta into LDS.
@@ -184,12 +181,18 @@ __global__ __launch_bounds__(256) void verify_step_kernel(VerifyParams p) {
     }
 
     // ---------------- the start state (gathered during the previous item when looping).
-    if (!looping) load_state(item, Sn);
     float4 S[R];
+    if (LOOP) {
 #pragma unroll
-    for (int j = 0; j < R; ++j) S[j] = Sn[j];
+      for (int j = 0; j < R; ++j) S[j] = Sn[j];
+    } else {
+      const float* src = p.pool + (static_cast<int64_t>(slot) * p.H + h) * head_elems +
+                         static_cast<int64_t>(row0) * D + v0 + 4 * cl;
+#pragma unroll
+      for (int j = 0; j < R; ++j) S[j] = *reinterpret_cast<const float4*>(src + j * D);
+    }
     __syncthreads();
-    if (looping) load_state(item + gridDim.x, Sn);
+    if (LOOP) load_state(item + gridDim.x, Sn);
 
     // ---------------- the T steps.
     for (int t = 0; t < T; ++t) {
@@ -283,6 +286,16 @@ __global__ __launch_bounds__(256) void verify_step_kernel(VerifyParams p) {
         }
       }
     }
+  };
+  if (LOOP) {
+    load_state(blockIdx.x, Sn);
+    for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+      if (item != static_cast<int>(blockIdx.x))
+        __syncthreads();   // the previous item's LDS tables are no longer read
+      run_item(item);
+    }
+  } else {
+    run_item(blockIdx.x);
   }
 }
 
@@ -302,9 +315,14 @@ hipError_t launch_verify_bv(const VerifyParams& p, hipStream_t s) {
   // The LDS limit for the largest step count is set once per device, not per call.
   static PerDeviceOnce attr_once;
   hipError_t e = attr_once.run([](int, int*) {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(&verify_step_kernel<BV, NORM>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                               static_cast<int>(verify_lds_bytes<BV, NORM>(KDA_MAX_STEPS_INTERNAL)));
+    const int bytes = static_cast<int>(verify_lds_bytes<BV, NORM>(KDA_MAX_STEPS_INTERNAL));
+    hipError_t r =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&verify_step_kernel<BV, NORM, false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (r == hipSuccess)
+      r = hipFuncSetAttribute(reinterpret_cast<const void*>(&verify_step_kernel<BV, NORM, true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    return r;
   });
   if (e != hipSuccess) return e;
   int cus = 0;
@@ -318,9 +336,12 @@ hipError_t launch_verify_bv(const VerifyParams& p, hipStream_t s) {
   // 33.7 -> 34.8, 45.6 -> 48.5 us; 32-column tiles at 448-960 items: 16.7 -> 24.6,
   // 31.3 -> 45.7 us).
   const int64_t items = static_cast<int64_t>(p.B) * p.H * (D / BV);
-  const bool loop = BV == D && cus > 0 && items >= 2 * static_cast<int64_t>(cus);
-  const dim3 grid(static_cast<unsigned>(loop ? cus : items));
-  hipLaunchKernelGGL((verify_step_kernel<BV, NORM>), grid, dim3(256), lds, s, p);
+  if (BV == D && cus > 0 && items >= 2 * static_cast<int64_t>(cus))
+    hipLaunchKernelGGL((verify_step_kernel<BV, NORM, true>), dim3(static_cast<unsigned>(cus)),
+                       dim3(256), lds, s, p);
+  else
+    hipLaunchKernelGGL((verify_step_kernel<BV, NORM, false>), dim3(static_cast<unsigned>(items)),
+                       dim3(256), lds, s, p);
   return hipGetLastError();
 }
 
